@@ -1,0 +1,207 @@
+/*
+ * moe.h — C ABI of the quantized routed mixture-of-experts FFN layer on
+ * MI355X (gfx950).
+ *
+ * The layer is the routed-expert FFN of the DeepSeek V4 Flash model described
+ * on "DeepSeek V4 Flash — DFlash Integration" (section Model Architecture:
+ * hidden 4096, 256 routed experts top-6 plus 1 shared expert, expert FFN
+ * 2048; hash routing by token id on the first layers, top-k over a learned
+ * router with optional bias elsewhere).  Per token it computes:
+ *
+ *   route   learned: logits l = x.W_r (fp64 pairwise sum, rounded to fp32),
+ *           scores s = sigmoid(l), key = s + bias, the top-k keys select the
+ *           experts and their weights are s / sum(selected s); hash: the
+ *           token's row of a fixed table, weights 1/k.  ("DeepSeek V4 Flash —
+ *           DFlash Integration", Monolithic HIP: keep the highest-ranked N
+ *           experts and renormalise; "ds4: dfm Edition": router top-k
+ *           returning selected IDs and normalized weights.)
+ *   quant   x split in 32-blocks, each quantized to int8 with an fp32 scale
+ *           d = amax/127, q = rint(x/d) ("DwarfStar (ds4) — ROCm / gfx1151
+ *           fork", Performance optimizations: the "preq" q8_0 kernels take
+ *           pre-quantized activations).
+ *   expert  g = Wg.x, u = Wu.x with int32 sums per weight block times the two
+ *           block scales, h = SiLU(g)*u, h re-quantized per 32-block,
+ *           y = Wd.h; out = sum over selected experts of w_e*y_e plus the
+ *           shared expert's y ("DwarfStar (ds4) — ROCm / gfx1151 fork",
+ *           Performance optimizations: moe_gate_up_mid_* and moe_down_sum6
+ *           kernels; Model Weights: routed experts 2-bit, shared experts Q8).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees them and keeps no reference after a call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    work on it and return without synchronising, except where stated.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    rejected call returns a negative moe_status and enqueues nothing.
+ *    Launch failures return MOE_ERR_HIP.  Device-side faults, if any, appear
+ *    at the caller's next synchronisation.
+ *  - Calls sharing one workspace must not overlap (same stream, or ordered).
+ */
+#ifndef QRMOE_MOE_H
+#define QRMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_TOKENS 16384 /* tokens per call; larger batches are refused, not split */
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,     /* NULL/misaligned/overlapping pointer, bad enum, k > E ... */
+    MOE_ERR_UNSUPPORTED = -2,     /* shape outside the compiled set (see moe_shape) */
+    MOE_ERR_TOO_MANY_TOKENS = -3, /* tokens > MOE_MAX_TOKENS */
+    MOE_ERR_WORKSPACE = -4,       /* workspace smaller than moe_workspace_bytes() or misaligned */
+    MOE_ERR_HIP = -5,             /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_BAD_TABLE = -6,       /* hash table entry out of range or repeated within a row */
+    MOE_ERR_BAD_TOKEN = -7        /* a token id outside [0, vocab) was seen (moe_workspace_flags) */
+} moe_status;
+
+/* Weight storage formats (canonical, little-endian, row-major [rows][cols]):
+ *  MOE_FMT_Q8_32  : per 32 weights one 34-byte block: fp16 d, int8 q[32];
+ *                   weight = d*q.  (q8_0-style, "DwarfStar (ds4) — ROCm /
+ *                   gfx1151 fork", Performance optimizations.)
+ *  MOE_FMT_Q2_256 : per 256 weights one 84-byte superblock: fp16 d, fp16
+ *                   dmin, uint8 sm[16], uint8 qs[64]; weight i has 2-bit code
+ *                   q = (qs[i/4] >> 2*(i%4)) & 3 and, with j = i/16,
+ *                   s = sm[j] & 15, m = sm[j] >> 4, weight = d*s*q - dmin*m.
+ *                   (2-bit routed experts: same page, Model Weights.)
+ * Forward calls read weights only in the PACKED layout that moe_pack_weights
+ * produces from the canonical one (same byte count). */
+enum { MOE_FMT_Q8_32 = 1, MOE_FMT_Q2_256 = 2 };
+enum { MOE_ROUTE_LEARNED = 1, MOE_ROUTE_HASH = 2 };
+
+/* Layer shape.  Supported: hidden H and ffn F powers of two in [128, 4096]
+ * (Q8_32; Q2_256 needs [512, 4096]); 1 <= top_k <= 8; top_k <= n_experts
+ * <= 1024; vocab >= 1 for hash routing. */
+typedef struct moe_shape {
+    int32_t hidden;     /* H */
+    int32_t n_experts;  /* E routed experts */
+    int32_t top_k;      /* k experts per token */
+    int32_t ffn;        /* F, routed and shared experts */
+    int32_t has_shared; /* 1: one always-on shared expert (Q8_32), weight 1 */
+    int32_t routed_fmt; /* MOE_FMT_* of the routed experts */
+    int32_t route;      /* MOE_ROUTE_* */
+    int32_t vocab;      /* rows of the hash table (hash routing) */
+} moe_shape;
+
+/* Layer weights, all device pointers, 16-byte aligned. */
+typedef struct moe_weights {
+    const float *router_w;     /* learned: [E][H] fp32 */
+    const float *router_b;     /* learned: [E] fp32, or NULL for no bias */
+    const int32_t *hash_table; /* hash: [vocab][k] int32 expert ids */
+    const void *gate;          /* packed bank of E matrices [F][H] in routed_fmt */
+    const void *up;            /* packed bank of E matrices [F][H] in routed_fmt */
+    const void *down;          /* packed bank of E matrices [H][F] in routed_fmt */
+    const void *sh_gate;       /* packed Q8_32 [F][H]; NULL iff has_shared == 0 */
+    const void *sh_up;         /* packed Q8_32 [F][H] */
+    const void *sh_down;       /* packed Q8_32 [H][F] */
+} moe_weights;
+
+/* Optional copies of intermediate results for verification (device
+ * pointers; any may be NULL).  Pair index p = t*k + j for the j-th selected
+ * expert of token t (rank order), p = T*k + t for the shared expert. */
+typedef struct moe_debug {
+    int32_t *ids;      /* [T][k] selected experts, rank order */
+    float *w;          /* [T][k] combine weights */
+    float *logits;     /* [T][E] router logits (learned) */
+    int8_t *xq;        /* [T][H] quantized x */
+    float *xd;         /* [T][H/32] x block scales */
+    int32_t *counts;   /* [E] pairs per expert */
+    int32_t *offsets;  /* [E+1] exclusive prefix of counts */
+    int32_t *perm;     /* [T*k] pairs grouped by expert, increasing p within an expert */
+    int8_t *hq;        /* [P][F] quantized h, P = T*k + T*has_shared */
+    float *hd;         /* [P][F/32] h block scales */
+    /* Exact integer block sums of sampled weight rows (rows r with
+     * r % sum_row_stride == 0, stride a power of two <= 32): Q8 per 32-block,
+     * Q2 per 16-weight subblock.  gate_sums/up_sums [P][F/stride][W_h],
+     * down_sums [P][H/stride][W_f] with W_h = H/16, W_f = F/16 when the routed
+     * experts are Q2_256 and H/32, F/32 otherwise; a Q8_32 pair (the shared
+     * expert) fills the first H/32 (F/32) entries of its row. */
+    int32_t *gate_sums;
+    int32_t *up_sums;
+    int32_t *down_sums;
+    int32_t sum_row_stride; /* >= 1 when any *_sums pointer is set */
+} moe_debug;
+
+int moe_abi_version(void);
+const char *moe_status_string(int status);
+
+/* Bytes of one matrix [rows][cols] in fmt (canonical and packed layouts have
+ * the same size), or -1 when cols does not fit the format. */
+int64_t moe_matrix_bytes(int32_t fmt, int64_t rows, int64_t cols);
+
+/* Repack n_mats canonical matrices [rows][cols] (back to back) into the
+ * library's packed layout.  canonical and packed are device buffers of
+ * n_mats*moe_matrix_bytes() bytes, 16-byte aligned, not overlapping.  This is
+ * the load-time step that builds the aligned weight artifacts ("ds4: dfm
+ * Edition", About this fork: aligned SoA artifacts built in-process at load). */
+int moe_pack_weights(int32_t fmt, const void *canonical, void *packed, int64_t n_mats, int64_t rows, int64_t cols,
+                     void *stream);
+
+/* Check a hash table on the device: every entry in [0, n_experts) and no
+ * expert twice in a row.  Synchronises `stream`.  Needs a workspace of at
+ * least 256 bytes.  Returns MOE_OK or MOE_ERR_BAD_TABLE with the first bad
+ * row in *bad_row (host pointer, may be NULL). */
+int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t top_k, int32_t n_experts, void *workspace,
+                         size_t workspace_bytes, int32_t *bad_row, void *stream);
+
+/* Device workspace bytes a forward call with `tokens` tokens needs (0 when
+ * the shape is unsupported).  Monotone in tokens, so a workspace sized for
+ * the largest batch serves every smaller one.  256-byte alignment required. */
+size_t moe_workspace_bytes(const moe_shape *shape, int32_t tokens);
+
+/* The layer: out[T][H] (fp32, overwritten) from x[T][H] (fp32).  token_ids
+ * [T] int32 is required for hash routing and ignored otherwise.  out must not
+ * overlap x.  tokens == 0 is a no-op (pointers may then be NULL).  The
+ * workspace must have been initialised (moe_workspace_init).
+ * Token ids outside [0, vocab) are clamped to row 0 of the table and
+ * recorded in the workspace flags (see moe_workspace_flags). */
+int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const float *x, const int32_t *token_ids,
+                      int32_t tokens, float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Same computation, plus copies of intermediates into `dbg`. */
+int moe_layer_forward_debug(const moe_shape *shape, const moe_weights *weights, const float *x,
+                            const int32_t *token_ids, int32_t tokens, float *out, void *workspace,
+                            size_t workspace_bytes, const moe_debug *dbg, void *stream);
+
+/* Zero a workspace's control words (work-list length, sticky flags).
+ * Required once after allocating a workspace, before its first forward call. */
+int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* Read the sticky device-side flags of a workspace: bit 0 = a token id was
+ * outside [0, vocab), bit 1 = a hash-table entry was outside [0, E).  They
+ * stay set until moe_workspace_init.  Synchronises `stream`. */
+int moe_workspace_flags(void *workspace, int32_t *flags, void *stream);
+
+/* Per-stage timing with HIP events.  While a profiler is attached to the
+ * calling thread, every kernel a forward call launches is bracketed by two
+ * events on the call's stream.  moe_prof_collect waits for the recorded
+ * events, adds the elapsed milliseconds and launch counts per stage into the
+ * caller's arrays (n_stages entries, index = stage id) and forgets them. */
+typedef struct moe_prof moe_prof;
+enum {
+    MOE_STAGE_ROUTE = 0,   /* decode batches: quantize x + router logits in one kernel */
+    MOE_STAGE_QUANT = 1,   /* batched: activation quantizer */
+    MOE_STAGE_LOGITS = 2,  /* batched: router logits */
+    MOE_STAGE_SELECT = 3,  /* top-k / hash selection (decode batches: + sort and work list) */
+    MOE_STAGE_SORT = 4,    /* batched: token sort into per-expert work lists */
+    MOE_STAGE_GATEUP = 5,  /* expert gate/up + SwiGLU + quantize h */
+    MOE_STAGE_DOWN = 6,    /* expert down projection, weighted per pair */
+    MOE_STAGE_COMBINE = 7, /* sum over each token's experts (ascending id) + shared */
+    MOE_N_STAGES = 8
+};
+const char *moe_stage_name(int32_t stage);
+int moe_prof_create(moe_prof **prof, int32_t max_events);
+void moe_prof_destroy(moe_prof *prof);
+int moe_prof_attach(moe_prof *prof); /* NULL detaches */
+int moe_prof_collect(moe_prof *prof, float *stage_ms, int32_t *stage_launches, int32_t n_stages);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

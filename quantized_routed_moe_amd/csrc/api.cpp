@@ -1,0 +1,351 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout, kernel dispatch and per-stage event timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+
+using namespace qrmoe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMfmaTile = 64;  // tokens per MFMA work tile
+
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int validate_shape(const moe_shape *s) {
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->routed_fmt != MOE_FMT_Q8_32 && s->routed_fmt != MOE_FMT_Q2_256) return MOE_ERR_INVALID_ARG;
+    if (s->route != MOE_ROUTE_LEARNED && s->route != MOE_ROUTE_HASH) return MOE_ERR_INVALID_ARG;
+    if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_INVALID_ARG;
+    if (s->top_k < 1 || s->n_experts < s->top_k) return MOE_ERR_INVALID_ARG;
+    if (s->route == MOE_ROUTE_HASH && s->vocab < 1) return MOE_ERR_INVALID_ARG;
+    if (s->top_k > 8 || s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
+    const int lo = s->routed_fmt == MOE_FMT_Q2_256 ? 512 : 128;
+    if (!pow2(s->hidden) || !pow2(s->ffn) || s->hidden < lo || s->ffn < lo || s->hidden > 4096 || s->ffn > 4096)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// Upper bound of the work-list length: sum over experts of ceil(n_e / G)
+// with sum n_e = P and at most min(E, P) non-empty experts, plus the shared
+// expert's ceil(T / G) groups.
+int64_t max_groups(const moe_shape *s, int64_t T, int64_t G) {
+    const int64_t P = T * s->top_k;
+    const int64_t active = P < s->n_experts ? P : s->n_experts;
+    return (P + active * (G - 1)) / G + (s->has_shared ? (T + G - 1) / G : 0);
+}
+
+struct Layout {
+    size_t ctl, logits, ids, w, xq, xd, xs16, counts, offsets, perm, groups, hq, hd, y, total;
+};
+
+
+Layout make_layout(const moe_shape *s, int64_t T) {
+    const int64_t H = s->hidden, E = s->n_experts, k = s->top_k, F = s->ffn;
+    const int64_t P = T * k + (s->has_shared ? T : 0);
+    int64_t G = max_groups(s, T, kVecTok);
+    const int64_t G2 = max_groups(s, T, kMfmaTile);
+    if (G2 > G) G = G2;
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o += up(bytes == 0 ? 1 : bytes);
+        return at;
+    };
+    L.ctl = take(kCtlWords * 4);
+    L.logits = take(T * E * 4);
+    L.ids = take(T * k * 4);
+    L.w = take(T * k * 4);
+    L.xq = take(T * H);
+    L.xd = take(T * (H / 32) * 4);
+    L.xs16 = take(T * (H / 16) * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.perm = take(T * k * 4);
+    L.groups = take(G * 16);
+    L.hq = take(P * F);
+    L.hd = take(P * (F / 32) * 4);
+    L.y = take(P * H * 4);
+    L.total = o;
+    return L;
+}
+
+struct EventPair {
+    hipEvent_t a, b;
+    int stage;
+};
+
+}  // namespace
+
+struct moe_prof {
+    std::vector<hipEvent_t> pool;
+    std::vector<EventPair> used;
+    size_t next = 0;
+};
+
+static thread_local moe_prof *t_prof = nullptr;
+
+namespace {
+
+// Launch helper: brackets the launch with events when a profiler is attached.
+template <class F>
+hipError_t timed(int stage, hipStream_t s, F &&launch) {
+    moe_prof *p = t_prof;
+    EventPair ev{nullptr, nullptr, stage};
+    if (p && p->next + 2 <= p->pool.size()) {
+        ev.a = p->pool[p->next++];
+        ev.b = p->pool[p->next++];
+        hipEventRecord(ev.a, s);
+    }
+    hipError_t err = launch();
+    if (ev.a) {
+        hipEventRecord(ev.b, s);
+        p->used.push_back(ev);
+    }
+    return err;
+}
+
+int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x, const int32_t *token_ids,
+                 int32_t tokens, float *out, void *workspace, size_t ws_bytes, const moe_debug *dbg, void *stream) {
+    int st = validate_shape(shape);
+    if (st != MOE_OK) return st;
+    if (tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (tokens > MOE_MAX_TOKENS) return MOE_ERR_TOO_MANY_TOKENS;
+    if (tokens == 0) return MOE_OK;  // empty batch: nothing is read or written, buffers may be NULL
+    if (!wts || !x || !out || !workspace) return MOE_ERR_INVALID_ARG;
+    const bool learned = shape->route == MOE_ROUTE_LEARNED;
+    if (learned && !wts->router_w) return MOE_ERR_INVALID_ARG;
+    if (!learned && (!wts->hash_table || !token_ids)) return MOE_ERR_INVALID_ARG;
+    if (!wts->gate || !wts->up || !wts->down) return MOE_ERR_INVALID_ARG;
+    if (shape->has_shared && (!wts->sh_gate || !wts->sh_up || !wts->sh_down)) return MOE_ERR_INVALID_ARG;
+    if (!shape->has_shared && (wts->sh_gate || wts->sh_up || wts->sh_down)) return MOE_ERR_INVALID_ARG;
+    const void *al16[] = {x, out, wts->router_w, wts->gate, wts->up, wts->down, wts->sh_gate, wts->sh_up, wts->sh_down};
+    for (const void *p : al16)
+        if (p && !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
+    const int64_t T = tokens, H = shape->hidden;
+    {
+        const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out, n = (uintptr_t)(T * H * 4);
+        if (T > 0 && xa < oa + n && oa < xa + n) return MOE_ERR_INVALID_ARG;
+    }
+    if (dbg && (dbg->gate_sums || dbg->up_sums || dbg->down_sums) &&
+        (!pow2(dbg->sum_row_stride) || dbg->sum_row_stride > shape->ffn || dbg->sum_row_stride > shape->hidden))
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(shape, T);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)workspace;
+    LayerArgs a{};
+    a.d = Dims{(int32_t)T, shape->hidden, shape->n_experts, shape->top_k, shape->ffn, shape->has_shared,
+               shape->routed_fmt, shape->route, shape->vocab,
+               (int32_t)(T * shape->top_k + (shape->has_shared ? T : 0))};
+    a.wt = Weights{wts->router_w, wts->router_b, wts->hash_table, (const uint8_t *)wts->gate,
+                   (const uint8_t *)wts->up, (const uint8_t *)wts->down, (const uint8_t *)wts->sh_gate,
+                   (const uint8_t *)wts->sh_up, (const uint8_t *)wts->sh_down};
+    a.ws = Ws{(int32_t *)(base + L.ctl), (float *)(base + L.logits), (int32_t *)(base + L.ids),
+              (float *)(base + L.w), (int8_t *)(base + L.xq), (float *)(base + L.xd),
+              (int32_t *)(base + L.xs16), (int32_t *)(base + L.counts), (int32_t *)(base + L.offsets),
+              (int32_t *)(base + L.perm), (int4 *)(base + L.groups), (int8_t *)(base + L.hq),
+              (float *)(base + L.hd), (float *)(base + L.y)};
+    const bool dump = dbg && (dbg->gate_sums || dbg->up_sums || dbg->down_sums);
+    const bool q2 = shape->routed_fmt == MOE_FMT_Q2_256;
+    a.dump = Dump{dump ? dbg->gate_sums : nullptr, dump ? dbg->up_sums : nullptr, dump ? dbg->down_sums : nullptr,
+                  dump ? dbg->sum_row_stride : 1, (int32_t)(q2 ? H / 16 : H / 32),
+                  (int32_t)(q2 ? shape->ffn / 16 : shape->ffn / 32)};
+    a.x = x;
+    a.token_ids = token_ids;
+    a.out = out;
+
+    hipError_t err = hipSuccess;
+    auto run = [&](int stage, auto &&fn) {
+        if (err == hipSuccess) err = timed(stage, s, fn);
+    };
+    const int64_t mg = max_groups(shape, T, kVecTok);
+    if (T <= kDecodeMaxT) {
+        a.group_tok = kVecTok;
+        run(MOE_STAGE_ROUTE, [&] { return launch_route_decode(a, s); });
+        run(MOE_STAGE_SELECT, [&] { return launch_select_sort(a, s); });
+        run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, dump, s); });
+        run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
+        run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
+    } else {
+        a.group_tok = kVecTok;
+        run(MOE_STAGE_QUANT, [&] { return launch_quant(a, s); });
+        if (learned) run(MOE_STAGE_LOGITS, [&] { return launch_logits(a, s); });
+        run(MOE_STAGE_SELECT, [&] { return launch_select(a, s); });
+        run(MOE_STAGE_SORT, [&] { return launch_sort(a, s); });
+        run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, dump, s); });
+        run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
+        run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
+    }
+    if (err == hipSuccess && dbg) {
+        const int64_t E = shape->n_experts, k = shape->top_k, F = shape->ffn, P = a.d.P;
+        auto cp = [&](void *dst, const void *src, size_t n) {
+            if (dst && err == hipSuccess) err = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s);
+        };
+        cp(dbg->ids, a.ws.ids, T * k * 4);
+        cp(dbg->w, a.ws.w, T * k * 4);
+        if (learned) cp(dbg->logits, a.ws.logits, T * E * 4);
+        cp(dbg->xq, a.ws.xq, T * H);
+        cp(dbg->xd, a.ws.xd, T * (H / 32) * 4);
+        cp(dbg->counts, a.ws.counts, E * 4);
+        cp(dbg->offsets, a.ws.offsets, (E + 1) * 4);
+        cp(dbg->perm, a.ws.perm, T * k * 4);
+        cp(dbg->hq, a.ws.hq, P * F);
+        cp(dbg->hd, a.ws.hd, P * (F / 32) * 4);
+    }
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_TOO_MANY_TOKENS: return "too many tokens";
+        case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_BAD_TABLE: return "invalid hash table";
+        case MOE_ERR_BAD_TOKEN: return "token id out of range";
+        default: return "unknown status";
+    }
+}
+
+int64_t moe_matrix_bytes(int32_t fmt, int64_t rows, int64_t cols) {
+    if (rows < 0 || cols <= 0) return -1;
+    if (fmt == MOE_FMT_Q8_32 && cols % 32 == 0) return q8_bytes(rows, cols);
+    if (fmt == MOE_FMT_Q2_256 && cols % 256 == 0) return q2_bytes(rows, cols);
+    return -1;
+}
+
+int moe_pack_weights(int32_t fmt, const void *canonical, void *packed, int64_t n_mats, int64_t rows, int64_t cols,
+                     void *stream) {
+    const int64_t mb = moe_matrix_bytes(fmt, rows, cols);
+    if (mb < 0 || n_mats < 0 || !canonical || !packed) return MOE_ERR_INVALID_ARG;
+    if (!aligned(canonical, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
+    const uintptr_t c = (uintptr_t)canonical, p = (uintptr_t)packed, n = (uintptr_t)(n_mats * mb);
+    if (n > 0 && c < p + n && p < c + n) return MOE_ERR_INVALID_ARG;
+    if (n_mats == 0 || rows == 0) return MOE_OK;
+    hipError_t err = launch_pack(fmt, (const uint8_t *)canonical, (uint8_t *)packed, n_mats, rows, cols,
+                                 (hipStream_t)stream);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t top_k, int32_t n_experts, void *workspace,
+                         size_t workspace_bytes, int32_t *bad_row, void *stream) {
+    if (!table || !workspace || vocab < 1 || top_k < 1 || top_k > 8 || n_experts < top_k) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < 256 || !aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t *res = (int32_t *)workspace + (kCtlWords - 1);  // scratch word of the ctl area, never a counter
+    if (workspace_bytes < (size_t)kCtlWords * 4) res = (int32_t *)workspace;
+    hipError_t err = launch_check_table(table, vocab, top_k, n_experts, res, s);
+    int32_t host = 0;
+    if (err == hipSuccess) err = hipMemcpyAsync(&host, res, 4, hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    if (bad_row) *bad_row = host == INT32_MAX ? -1 : host;
+    return host == INT32_MAX ? MOE_OK : MOE_ERR_BAD_TABLE;
+}
+
+size_t moe_workspace_bytes(const moe_shape *shape, int32_t tokens) {
+    if (validate_shape(shape) != MOE_OK || tokens < 0 || tokens > MOE_MAX_TOKENS) return 0;
+    return make_layout(shape, tokens).total;
+}
+
+int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace || !aligned(workspace, kAlign)) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < (size_t)kCtlWords * 4) return MOE_ERR_WORKSPACE;
+    hipError_t err = launch_ws_init((int32_t *)workspace, kCtlWords, (hipStream_t)stream);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_workspace_flags(void *workspace, int32_t *flags, void *stream) {
+    if (!workspace || !flags || !aligned(workspace, kAlign)) return MOE_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t *dev = (int32_t *)workspace + kCtlFlags;
+    int32_t host = 0;
+    hipError_t err = hipMemcpyAsync(&host, dev, 4, hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    *flags = host;
+    return MOE_OK;
+}
+
+int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const float *x, const int32_t *token_ids,
+                      int32_t tokens, float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(shape, weights, x, token_ids, tokens, out, workspace, workspace_bytes, nullptr, stream);
+}
+
+int moe_layer_forward_debug(const moe_shape *shape, const moe_weights *weights, const float *x,
+                            const int32_t *token_ids, int32_t tokens, float *out, void *workspace,
+                            size_t workspace_bytes, const moe_debug *dbg, void *stream) {
+    if (!dbg) return MOE_ERR_INVALID_ARG;
+    return forward_impl(shape, weights, x, token_ids, tokens, out, workspace, workspace_bytes, dbg, stream);
+}
+
+const char *moe_stage_name(int32_t stage) {
+    static const char *names[MOE_N_STAGES] = {"route", "quant", "logits", "select", "sort", "gateup", "down", "combine"};
+    return (stage >= 0 && stage < MOE_N_STAGES) ? names[stage] : "?";
+}
+
+int moe_prof_create(moe_prof **prof, int32_t max_events) {
+    if (!prof || max_events < 2) return MOE_ERR_INVALID_ARG;
+    moe_prof *p = new moe_prof();
+    p->pool.resize((size_t)max_events);
+    for (auto &e : p->pool) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto &f : p->pool)
+                if (f) hipEventDestroy(f);
+            delete p;
+            return MOE_ERR_HIP;
+        }
+    }
+    *prof = p;
+    return MOE_OK;
+}
+
+void moe_prof_destroy(moe_prof *prof) {
+    if (!prof) return;
+    if (t_prof == prof) t_prof = nullptr;
+    for (auto &e : prof->pool) hipEventDestroy(e);
+    delete prof;
+}
+
+int moe_prof_attach(moe_prof *prof) {
+    t_prof = prof;
+    return MOE_OK;
+}
+
+int moe_prof_collect(moe_prof *prof, float *stage_ms, int32_t *stage_launches, int32_t n_stages) {
+    if (!prof || !stage_ms || !stage_launches || n_stages < 1) return MOE_ERR_INVALID_ARG;
+    for (auto &ev : prof->used) {
+        if (hipEventSynchronize(ev.b) != hipSuccess) return MOE_ERR_HIP;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ev.a, ev.b) != hipSuccess) return MOE_ERR_HIP;
+        if (ev.stage < n_stages) {
+            stage_ms[ev.stage] += ms;
+            stage_launches[ev.stage] += 1;
+        }
+    }
+    prof->used.clear();
+    prof->next = 0;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// Internal definitions shared by the HIP kernels and the host dispatcher of
+// the routed-MoE layer (gfx950, wave64).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qrmoe {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;       // every kernel runs 4 waves per workgroup
+constexpr int kVecTok = 8;          // tokens per work group of the VALU expert kernels
+constexpr int kVecRows = 32;        // weight rows per workgroup of the VALU expert kernels (= one h block)
+constexpr int kDecodeMaxT = 32;     // batches up to this size use the fused decode routing kernel
+constexpr int kFmtQ8 = 1, kFmtQ2 = 2;
+constexpr int kRouteLearned = 1, kRouteHash = 2;
+
+// ctl[] words of the workspace
+enum : int { kCtlGroups = 1, kCtlFlags = 2, kCtlMagic = 3 };
+constexpr int kCtlWords = 64;
+constexpr int32_t kWsMagic = 0x4F4D5251;  // set by moe_workspace_init
+
+// ------------------------------------------------------------------------
+// Packed weight layouts (what moe_pack_weights writes; same byte count as the
+// canonical AoS blocks):
+//   Q8 matrix [R][K]: int8 codes plane R*K (row-major), then fp16 scale plane
+//                     R*(K/32) (row-major).
+//   Q2 matrix [R][K]: codes plane R*K/4 bytes, then scale/min plane R*K/16
+//                     bytes (same nibble order as canonical sm), then the
+//                     (fp16 d, fp16 dmin) plane R*(K/256)*4 bytes.  In the
+//                     codes plane each 32-bit word holds one 16-weight
+//                     subblock: byte c, bits [2s, 2s+2) hold the code of
+//                     weight 4s + c, so (word >> 2s) & 0x03030303 yields the
+//                     codes of weights 4s..4s+3 in bytes 0..3.
+// ------------------------------------------------------------------------
+__host__ __device__ inline int64_t q8_bytes(int64_t R, int64_t K) { return R * K + R * (K / 32) * 2; }
+__host__ __device__ inline int64_t q2_bytes(int64_t R, int64_t K) { return R * K / 4 + R * K / 16 + R * (K / 256) * 4; }
+__host__ __device__ inline int64_t mat_bytes(int fmt, int64_t R, int64_t K) {
+    return fmt == kFmtQ8 ? q8_bytes(R, K) : q2_bytes(R, K);
+}
+
+struct Dims {
+    int32_t T, H, E, k, F, has_shared, fmt, route, vocab;
+    int32_t P;  // pairs including the shared expert's: T*k + T*has_shared
+};
+
+// Workspace pointers (device).
+struct Ws {
+    int32_t *ctl;
+    float *logits;
+    int32_t *ids;
+    float *w;
+    int8_t *xq;
+    float *xd;
+    int32_t *xs16;   // [T][H/16] sums of xq over 16-subblocks (Q2 experts)
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+    int4 *groups;    // {expert (E = shared), first index into perm (or first token), count, 0}
+    int8_t *hq;
+    float *hd;
+    float *y;        // [P][H] weighted expert outputs (w already applied)
+};
+
+struct Weights {
+    const float *router_w, *router_b;
+    const int32_t *table;
+    const uint8_t *gate, *up, *down;
+    const uint8_t *sh_gate, *sh_up, *sh_down;
+};
+
+struct Dump {
+    int32_t *gate_sums, *up_sums, *down_sums;
+    int32_t stride;           // sampled rows: r % stride == 0
+    int32_t pitch_gu, pitch_dn;  // int32 entries per sampled row (H/32 or H/16, F/32 or F/16)
+};
+
+struct LayerArgs {
+    Dims d;
+    Weights wt;
+    Ws ws;
+    Dump dump;
+    const float *x;
+    const int32_t *token_ids;
+    float *out;
+    int32_t group_tok;  // tokens per group in the work list (kVecTok or the MFMA tile)
+};
+
+// ------------------------------------------------------------------ device
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (each weight byte is used once per call).
+__device__ __forceinline__ int4 load_stream16(const void *p) {
+    const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(p));
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+
+// Per-32-block quantizer: d = amax/127, q = clamp(rint(v * (1/d)), +-127);
+// amax == 0 gives d = 0, q = 0.  Same definition as the layer's activation
+// quantizer for x and h.
+__device__ __forceinline__ float quant_scale(float amax) { return amax / 127.0f; }
+__device__ __forceinline__ int quant_code(float v, float inv) {
+    float r = rintf(v * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// Exclusive scan of n <= 1024 ints in LDS (in place into `out`), 256 threads.
+__device__ inline void block_excl_scan(const int *in, int *out, int n, int *tmp_wave /*[4]*/, int *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int v[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int idx = tid * 4 + i;
+        v[i] = idx < n ? in[idx] : 0;
+        s += v[i];
+    }
+    int inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) tmp_wave[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += tmp_wave[w];
+    int run = base + inc - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int idx = tid * 4 + i;
+        if (idx < n) out[idx] = run;
+        run += v[i];
+    }
+    if (tid == 255) *total = run;
+    __syncthreads();
+}
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_pack(int fmt, const uint8_t *canon, uint8_t *packed, int64_t n_mats, int64_t rows, int64_t cols,
+                       hipStream_t s);
+hipError_t launch_check_table(const int32_t *table, int32_t vocab, int32_t k, int32_t E, int32_t *result,
+                              hipStream_t s);
+hipError_t launch_ws_init(int32_t *ctl, int64_t n_words, hipStream_t s);
+hipError_t launch_route_decode(const LayerArgs &a, hipStream_t s);
+hipError_t launch_select_sort(const LayerArgs &a, hipStream_t s);
+hipError_t launch_quant(const LayerArgs &a, hipStream_t s);
+hipError_t launch_logits(const LayerArgs &a, hipStream_t s);
+hipError_t launch_select(const LayerArgs &a, hipStream_t s);
+hipError_t launch_sort(const LayerArgs &a, hipStream_t s);
+hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool dump, hipStream_t s);
+hipError_t launch_down_vec(const LayerArgs &a, int max_groups, bool dump, hipStream_t s);
+hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
+hipError_t launch_gateup_mfma(const LayerArgs &a, int max_tiles, bool dump, hipStream_t s);
+hipError_t launch_down_mfma(const LayerArgs &a, int max_tiles, bool dump, hipStream_t s);
+
+}  // namespace qrmoe

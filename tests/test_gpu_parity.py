@@ -1,0 +1,256 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar (per the layer's contract): expert ids, combine weights, router logits,
+quantized activations, the token sort and every sampled int32 block sum are
+bit-exact; fp32 outputs agree within 2e-3 normwise (max |gpu - oracle| /
+max |oracle|).  h is quantized from fp32 values whose accumulation order
+differs between the GPU and the fp64 oracle, so its codes may differ by one
+step where a value sits on a rounding boundary; the stage-2 (down) sums are
+therefore checked with the GPU's own h codes fed to the oracle.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import moe_synth as ms
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+LOG = os.environ.get("MOE_PARITY_LOG")
+
+torch = pytest.importorskip("torch")
+
+
+def _qr():
+    import quantized_routed_moe_amd as qr
+    return qr
+
+
+_cache = {}
+
+
+def case(cfg):
+    """(inputs, layer) for a config; one large case stays resident at a time."""
+    if cfg not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        inp = ms.make_inputs(cfg)
+        layer = _qr().MoELayer(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared, cfg.routed_fmt, cfg.route,
+                               cfg.vocab if cfg.route == "hash" else 0).load(inp)
+        _cache[cfg] = (inp, layer)
+    return _cache[cfg]
+
+
+def log(name, **kv):
+    print(name, json.dumps(kv), flush=True)
+    if LOG:
+        with open(LOG, "a") as f:
+            f.write(json.dumps({"case": name, **kv}) + "\n")
+
+
+def run_gpu(cfg, inp, layer, x=None, tok=None, stride=0):
+    x = inp["x"] if x is None else x
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    tt = None
+    if cfg.route == "hash":
+        tok = inp["token_ids"] if tok is None else tok
+        tt = torch.from_numpy(np.ascontiguousarray(tok)).cuda()
+    r = layer.forward_debug(xt, tt, sum_row_stride=stride)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in r.items()}
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def check(cfg, inp, g, x=None, tok=None, rows=None, stride=0, name=""):
+    """Compare GPU results g with the oracle; rows = tokens to run the full oracle on."""
+    x = inp["x"] if x is None else x
+    T, H, E, k, F = x.shape[0], cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn
+    if cfg.route == "hash":
+        tok = inp["token_ids"] if tok is None else tok
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    # a1/a2: routing of every token, bit-exact
+    if cfg.route == "learned":
+        lo = oracle.router_logits(x, inp["router_w"])
+        assert np.array_equal(bits(g["logits"]), bits(lo)), "router logits differ"
+        ids_o, w_o, _ = oracle.route_learned(lo, inp["router_b"], k)
+    else:
+        ids_o, w_o = oracle.route_hash(tok, inp["hash_table"], E)
+    assert np.array_equal(g["ids"], ids_o), "expert selection differs"
+    assert np.array_equal(bits(g["w"]), bits(w_o)), "combine weights differ"
+    # a3: quantized x, bit-exact
+    xq_o, xd_o = oracle.quantize(x)
+    assert np.array_equal(g["xq"], xq_o) and np.array_equal(bits(g["xd"]), bits(xd_o)), "x quantization differs"
+    # a4: sort, bit-exact
+    c_o, off_o, perm_o = oracle.sort_pairs(ids_o, E)
+    assert np.array_equal(g["counts"], c_o) and np.array_equal(g["offsets"], off_o)
+    assert np.array_equal(g["perm"], perm_o), "token sort differs"
+    # a5/a6: outputs of the sampled tokens
+    o = oracle.forward(cfg, inp, x=x[rows], token_ids=tok[rows] if cfg.route == "hash" else None)
+    out_g, out_o = g["out"][rows], o["out"]
+    assert np.all(np.isfinite(out_g))
+    scale = float(np.max(np.abs(out_o)))
+    err = float(np.max(np.abs(out_g.astype(np.float64) - out_o))) / scale
+    # h codes of the sampled pairs: equal except single steps at rounding boundaries
+    S = k + 1 if cfg.shared else k
+    n_h, n_bad = 0, 0
+    for i, t in enumerate(rows):
+        for j in range(S):
+            p = t * k + j if j < k else T * k + t
+            hq_g, hq_o = g["hq"][p].astype(np.int32), o["hq"][i, j].astype(np.int32)
+            diff = np.abs(hq_g - hq_o)
+            assert diff.max() <= 1, "h codes differ by more than one step"
+            n_h += diff.size
+            n_bad += int(np.count_nonzero(diff))
+            np.testing.assert_allclose(g["hd"][p], o["hd"][i, j], rtol=2e-6, atol=0)
+    assert n_bad <= max(2, n_h // 1000), f"{n_bad} of {n_h} h codes differ"
+    # exact int32 block sums of sampled rows
+    if stride:
+        fmt = cfg.routed_fmt
+        for i, t in enumerate(rows[:4]):
+            for j in range(S):
+                p = t * k + j if j < k else T * k + t
+                if j < k:
+                    e = ids_o[t, j]
+                    mats, f = (inp["gate"][e], inp["up"][e], inp["down"][e]), fmt
+                else:
+                    mats, f = (inp["sh_gate"], inp["sh_up"], inp["sh_down"]), "q8"
+                nh = H // 32 if f == "q8" else H // 16
+                nf = F // 32 if f == "q8" else F // 16
+                for m, key in ((mats[0], "gate_sums"), (mats[1], "up_sums")):
+                    want = oracle.block_sums(m, f, F, H, xq_o[t])[::stride]
+                    assert np.array_equal(g[key][p][:, :nh], want), f"{key} differ (token {t}, slot {j})"
+                want = oracle.block_sums(mats[2], f, H, F, np.ascontiguousarray(g["hq"][p]))[::stride]
+                assert np.array_equal(g["down_sums"][p][:, :nf], want), f"down sums differ (token {t}, slot {j})"
+    log(name or cfg.name, T=T, rows=len(rows), err=err, h_code_steps=n_bad, h_codes=n_h)
+    assert err <= TOL, f"normwise output error {err:.3e} > {TOL}"
+
+
+# ------------------------------------------------------------- small cases
+SMALL = [
+    ms.CONFIGS["tiny"],
+    ms.LayerConfig("q8_learned_512", 512, 32, 4, 256, 7, seed=11),
+    ms.LayerConfig("q8_learned_512_T32", 512, 32, 4, 256, 32, seed=12),
+    ms.LayerConfig("q8_learned_512_T33", 512, 32, 4, 256, 33, seed=13),
+    ms.LayerConfig("q8_learned_512_T100", 512, 32, 4, 256, 100, seed=14),
+    ms.LayerConfig("q2_learned_512", 512, 32, 4, 512, 9, routed_fmt="q2", seed=15),
+    ms.LayerConfig("q2_learned_1024_T40", 1024, 24, 3, 512, 40, routed_fmt="q2", seed=16),
+    ms.LayerConfig("q8_hash_256", 256, 16, 2, 128, 3, route="hash", vocab=1000, seed=17),
+    ms.LayerConfig("q8_hash_256_T50", 256, 16, 2, 128, 50, route="hash", vocab=1000, seed=18),
+    ms.LayerConfig("q8_noshared_k1", 256, 8, 1, 256, 5, shared=False, seed=19),
+    ms.LayerConfig("q8_all_experts", 256, 8, 8, 128, 6, seed=20),
+    ms.LayerConfig("q8_nobias_T1", 1024, 64, 6, 512, 1, bias=False, seed=21),
+    ms.LayerConfig("q2_hash_T32", 512, 16, 6, 512, 32, routed_fmt="q2", route="hash", vocab=64, seed=22),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small_parity(cfg):
+    inp, layer = case(cfg)
+    g = run_gpu(cfg, inp, layer, stride=1)
+    check(cfg, inp, g, stride=1)
+
+
+def test_every_token_to_the_same_experts():
+    """Hash table with one row: all tokens hit the same k experts (groups split per 8 tokens)."""
+    cfg = ms.LayerConfig("hash_one_row", 512, 16, 6, 256, 32, route="hash", vocab=1, seed=23)
+    inp, layer = case(cfg)
+    g = run_gpu(cfg, inp, layer, stride=4)
+    assert sorted(np.nonzero(g["counts"])[0].tolist()) == sorted(inp["hash_table"][0].tolist())
+    check(cfg, inp, g, stride=4)
+
+
+def test_skewed_bias_sends_all_tokens_to_one_expert():
+    cfg = ms.LayerConfig("skew", 256, 16, 2, 128, 64, seed=24)
+    inp = ms.make_inputs(cfg)
+    inp["router_b"][5] = 10.0  # expert 5 wins every token
+    layer = _qr().MoELayer(256, 16, 2, 128).load(inp)
+    g = run_gpu(cfg, inp, layer, stride=2)
+    assert g["counts"][5] == 64
+    check(cfg, inp, g, stride=2, name="skew")
+
+
+def test_max_tokens_small_shape():
+    cfg = ms.LayerConfig("max_tokens", 256, 16, 2, 128, 16384, seed=25)
+    inp, layer = case(cfg)
+    g = run_gpu(cfg, inp, layer, stride=32)
+    rows = np.r_[0:3, 8191:8194, 16381:16384]
+    check(cfg, inp, g, rows=rows, stride=32)
+
+
+def test_empty_batch_is_a_no_op():
+    qr = _qr()
+    cfg = ms.CONFIGS["tiny"]
+    inp, layer = case(cfg)
+    x = torch.empty((0, cfg.hidden), dtype=torch.float32, device="cuda")
+    out = torch.empty((0, cfg.hidden), dtype=torch.float32, device="cuda")
+    layer.ensure_workspace(1)
+    qr.layer_forward(layer.shape, layer.weights(), x, None, out, layer.ws)
+
+
+# ------------------------------------------------ determinism / batching
+@pytest.mark.parametrize("cfg", [ms.LayerConfig("batch_learned", 512, 32, 4, 256, 12, seed=31),
+                                 ms.LayerConfig("batch_hash", 512, 32, 4, 256, 12, route="hash", vocab=300,
+                                                seed=32)], ids=lambda c: c.name)
+def test_batched_equals_single_token_calls_bitwise(cfg):
+    inp, layer = case(cfg)
+    x = torch.from_numpy(inp["x"]).cuda()
+    tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route == "hash" else None
+    full = layer.forward(x, tok).clone()
+    again = layer.forward(x, tok).clone()
+    assert torch.equal(full.view(torch.int32), again.view(torch.int32)), "two identical calls differ"
+    for t in range(cfg.tokens):
+        one = layer.forward(x[t:t + 1].contiguous(), tok[t:t + 1].contiguous() if tok is not None else None)
+        assert torch.equal(one.view(torch.int32), full[t:t + 1].view(torch.int32)), f"token {t} differs"
+
+
+# --------------------------------------------------------- error paths
+def test_out_of_range_token_id_is_flagged_not_faulted():
+    cfg = ms.LayerConfig("bad_token", 256, 16, 2, 128, 4, route="hash", vocab=100, seed=33)
+    inp, layer = case(cfg)
+    x = torch.from_numpy(inp["x"]).cuda()
+    tok = torch.tensor([1, 2, 100, -5], dtype=torch.int32, device="cuda")
+    out = layer.forward(x, tok)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert layer.flags() & 1
+
+
+def test_check_hash_table():
+    qr = _qr()
+    cfg = ms.LayerConfig("table", 256, 16, 2, 128, 4, route="hash", vocab=1000, seed=34)
+    inp, layer = case(cfg)
+    assert layer.check_table() == -1
+    bad = inp["hash_table"].copy()
+    bad[777, 1] = bad[777, 0]
+    layer.hash_table = torch.from_numpy(bad).cuda()
+    with pytest.raises(qr.MoEError) as ei:
+        layer.check_table()
+    assert "777" in str(ei.value)
+    layer.hash_table = torch.from_numpy(inp["hash_table"]).cuda()
+
+
+# ------------------------------------------------------ full-size layers
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["decode_q8", "decode_q2", "hash_decode"])
+def test_full_size_decode(name):
+    cfg = ms.CONFIGS[name]
+    inp, layer = case(cfg)
+    g = run_gpu(cfg, inp, layer, stride=64)
+    check(cfg, inp, g, stride=64)
+
+
+@pytest.mark.slow
+def test_full_size_prefill_sampled():
+    cfg = ms.CONFIGS["prefill"]
+    inp, layer = case(cfg)
+    g = run_gpu(cfg, inp, layer, stride=128)
+    rows = np.r_[0, 1, 2, 511, 1024, 1500, 2046, 2047, np.arange(37, 2048, 173)]
+    check(cfg, inp, g, rows=np.unique(rows), stride=128)
+    assert np.count_nonzero(g["counts"]) > 0
