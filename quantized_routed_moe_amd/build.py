@@ -12,9 +12,12 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libqrmoe.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "pack.hip", "route.hip", "expert_vec.hip"]
+SOURCES = ["api.cpp", "pack.hip", "route.hip", "expert_vec.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
+# -ffp-contract=off: floating-point operations round exactly as written (fused
+# multiply-adds only where the source asks for one), so every kernel that
+# shares a computation produces the same bits.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-I", os.path.join(ROOT, "include"),
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
 
 

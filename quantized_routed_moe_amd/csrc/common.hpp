@@ -12,7 +12,7 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;       // every kernel runs 4 waves per workgroup
 constexpr int kVecTok = 8;          // tokens per work group of the VALU expert kernels
 constexpr int kVecRows = 32;        // weight rows per workgroup of the VALU expert kernels (= one h block)
-constexpr int kDecodeMaxT = 32;     // batches up to this size use the fused decode routing kernel
+constexpr int kDecodeMaxT = 32;     // batches up to this size take the decode path
 constexpr int kFmtQ8 = 1, kFmtQ2 = 2;
 constexpr int kRouteLearned = 1, kRouteHash = 2;
 
@@ -61,6 +61,9 @@ struct Ws {
     int8_t *hq;
     float *hd;
     float *y;        // [P][H] weighted expert outputs (w already applied)
+    float *h;        // [P][F] SwiGLU output before quantization (decode batches)
+    float *scores;   // [T][E] sigmoid scores
+    float *keys;     // [T][E] selection keys (score + bias)
 };
 
 struct Weights {
@@ -124,6 +127,48 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
     return (int)r;
 }
 
+// One thread quantizes the 32-block `blk` of x into codes, scale and (when
+// xs16 is given) the two 16-subblock code sums.
+__device__ __forceinline__ void quant_one_block(const float *__restrict__ x, int8_t *__restrict__ xq,
+                                                float *__restrict__ xd, int32_t *__restrict__ xs16, int64_t blk) {
+    const float4 *src = reinterpret_cast<const float4 *>(x + blk * 32);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float4 f = src[i];
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float d = quant_scale(amax);
+    const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+    uint32_t words[8];
+    int s0 = 0, s1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            int q = quant_code(v[4 * i + c], inv);
+            if (i < 4) s0 += q; else s1 += q;
+            wv |= ((uint32_t)q & 0xffu) << (8 * c);
+        }
+        words[i] = wv;
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(xq + blk * 32);
+    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    xd[blk] = d;
+    if (xs16) {
+        xs16[2 * blk] = s0;
+        xs16[2 * blk + 1] = s1;
+    }
+}
+
 // Exclusive scan of n <= 1024 ints in LDS (in place into `out`), 256 threads.
 __device__ inline void block_excl_scan(const int *in, int *out, int n, int *tmp_wave /*[4]*/, int *total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -161,13 +206,15 @@ hipError_t launch_pack(int fmt, const uint8_t *canon, uint8_t *packed, int64_t n
 hipError_t launch_check_table(const int32_t *table, int32_t vocab, int32_t k, int32_t E, int32_t *result,
                               hipStream_t s);
 hipError_t launch_ws_init(int32_t *ctl, int64_t n_words, hipStream_t s);
-hipError_t launch_route_decode(const LayerArgs &a, hipStream_t s);
+hipError_t launch_decode_front(const LayerArgs &a, bool dump, hipStream_t s);
+hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s);
 hipError_t launch_select_sort(const LayerArgs &a, hipStream_t s);
+hipError_t launch_decode_down1(const LayerArgs &a, bool dump, hipStream_t s);
 hipError_t launch_quant(const LayerArgs &a, hipStream_t s);
 hipError_t launch_logits(const LayerArgs &a, hipStream_t s);
 hipError_t launch_select(const LayerArgs &a, hipStream_t s);
 hipError_t launch_sort(const LayerArgs &a, hipStream_t s);
-hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool dump, hipStream_t s);
+hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool skip_shared, bool dump, hipStream_t s);
 hipError_t launch_down_vec(const LayerArgs &a, int max_groups, bool dump, hipStream_t s);
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gateup_mfma(const LayerArgs &a, int max_tiles, bool dump, hipStream_t s);

@@ -1,0 +1,307 @@
+// Decode-sized batches (T <= 32 tokens).
+//
+//  front   quantize x and compute the router logits, scores and selection
+//          keys (learned layers: one workgroup per logit, the four waves each
+//          sum a quarter of the adjacent-pair tree), while further workgroups
+//          stream the shared expert's gate/up rows, which need no routing,
+//          leaving its h in fp32.
+//  select  one workgroup: top-k or hash selection, sort, work list, and the
+//          quantization of the shared expert's h.
+//  gateup  routed experts' gate/up + SwiGLU + h quantization (expert_vec.hip).
+//  down    T == 1: one kernel computes every output row from all selected
+//          experts at once (each wave holds the row of every expert in
+//          registers, requested before anything else) and sums w * y in
+//          ascending expert id, shared last, with the same rounding steps as
+//          the batched down + combine.  T > 1: per-group down rows into y,
+//          then the combine kernel (expert_vec.hip).
+//
+// Stage boundaries are kernel boundaries: no device-scope fences, which on
+// this multi-XCD part write back and invalidate L2.
+#include "dev_route.hpp"
+#include "dev_vec.hpp"
+
+namespace qrmoe {
+
+// ------------------------------------------------------------------ front
+template <int H>
+struct FrontSmem {
+    VecSmem<H, kVecTok> vs;
+    double part[4];
+};
+
+template <int H, bool DUMP>
+__global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_lead) {
+    __shared__ FrontSmem<H> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Dims &d = a.d;
+    if ((int)blockIdx.x < n_lead) {
+        const int nblk = d.T * (H / 32);
+        for (int b = blockIdx.x * 256 + tid; b < nblk; b += n_lead * 256)
+            quant_one_block(a.x, a.ws.xq, a.ws.xd, d.fmt == kFmtQ2 ? a.ws.xs16 : nullptr, b);
+        if (d.route != kRouteLearned) return;
+        const int nlog = d.T * d.E;
+        if constexpr (H >= 256) {
+            // one logit per workgroup; wave w sums elements [w*H/4, (w+1)*H/4)
+            constexpr int SEG = H / 256;
+            for (int le = blockIdx.x; le < nlog; le += n_lead) {
+                const int t = le / d.E, e = le % d.E;
+                const int off = wave * (H / 4) + lane * SEG;
+                double v = segment_tree<SEG>(a.x + (int64_t)t * H + off, a.wt.router_w + (int64_t)e * H + off);
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+                if (lane == 0) sm.part[wave] = v;
+                __syncthreads();
+                if (tid == 0) {
+                    const float l = (float)((sm.part[0] + sm.part[1]) + (sm.part[2] + sm.part[3]));
+                    a.ws.logits[le] = l;
+                    score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
+                }
+                __syncthreads();
+            }
+        } else {
+            for (int le = blockIdx.x * 4 + wave; le < nlog; le += n_lead * 4) {
+                const int t = le / d.E, e = le % d.E;
+                const float l = wave_logit<H>(a.x + (int64_t)t * H, a.wt.router_w + (int64_t)e * H, lane);
+                if (lane == 0) {
+                    a.ws.logits[le] = l;
+                    score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
+                }
+            }
+        }
+        return;
+    }
+    // shared expert: ROWS rows x up to 8 tokens; quantize those tokens' x into LDS
+    constexpr int ROWS = GuRows<H, kFmtQ8>::v;
+    const int s = blockIdx.x - n_lead, nrc = d.F / ROWS;
+    const int rc = s % nrc, t0 = (s / nrc) * kVecTok;
+    const int cnt = min(kVecTok, d.T - t0);
+    for (int b = tid; b < cnt * (H / 32); b += 256) {
+        const int tok = b / (H / 32), blk = b % (H / 32);
+        quant_one_block(a.x + (int64_t)(t0 + tok) * H, sm.vs.aq[tok], sm.vs.ad[tok], nullptr, blk);
+    }
+    if (tid < cnt) sm.vs.pair[tid] = d.T * d.k + t0 + tid;
+    __syncthreads();
+    gateup_rows<H, kFmtQ8, kVecTok, ROWS, false, DUMP>(a, sm.vs, a.wt.sh_gate, a.wt.sh_up, cnt, rc * ROWS);
+}
+
+// ----------------------------------------------------------------- select
+// One workgroup: top-k (or hash lookup) of every token, stable sort of the
+// P = T*k <= 256 pairs by expert (rank = number of pairs with a smaller
+// expert, or the same expert and a smaller pair index), the work list
+// (each expert's pairs cut into runs of at most kVecTok, experts ascending,
+// then the shared expert's token runs), and the quantization of the shared
+// expert's h, which the front kernel left in fp32.
+struct SelectSmem {
+    int32_t ids[kDecodeMaxT * 8];
+    float w[kDecodeMaxT * 8];
+    int32_t perm[kDecodeMaxT * 8];
+    int32_t gpos[kDecodeMaxT * 8 + 1];
+    int32_t tmp[4];
+    int32_t ngroups;
+};
+
+__global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
+    __shared__ SelectSmem rs;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Dims &d = a.d;
+    const int P = d.T * d.k;
+    // waves 1..3 quantize the shared expert's h (independent of the routing)
+    // while wave 0 starts on the selection; for T > 1 all waves select
+    if (d.has_shared && wave > 0) {
+        const int nb = d.T * (d.F / 32);
+        const float *__restrict__ hsrc = a.ws.h;
+        int8_t *__restrict__ hq = a.ws.hq;
+        float *__restrict__ hd = a.ws.hd;
+#pragma unroll 4
+        for (int i = tid - 64; i < nb; i += 192) {
+            const int64_t p = (int64_t)d.T * d.k + i / (d.F / 32);
+            const int b = i % (d.F / 32);
+            quant_one_block(hsrc + p * d.F, hq + p * d.F, hd + p * (d.F / 32), nullptr, b);
+        }
+    }
+    for (int t = wave; t < d.T; t += 4) {
+        if (d.route == kRouteLearned)
+            select_keys_wave(a.ws.keys + (int64_t)t * d.E, a.ws.scores + (int64_t)t * d.E, d.E, d.k, rs.ids + t * d.k,
+                             rs.w + t * d.k, lane);
+        else
+            select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.E, d.k, rs.ids + t * d.k, rs.w + t * d.k,
+                             a.ws.ctl + kCtlFlags, lane);
+    }
+    __syncthreads();
+    if (tid < P) {
+        const int e = rs.ids[tid];
+        int rank = 0;
+        for (int q = 0; q < P; ++q) {
+            const int f = rs.ids[q];
+            rank += (f < e) || (f == e && q < tid);
+        }
+        rs.perm[rank] = tid;
+        a.ws.ids[tid] = e;
+        a.ws.w[tid] = rs.w[tid];
+    }
+    __syncthreads();
+    int flag = 0;
+    if (tid < P) {
+        const int e = rs.ids[rs.perm[tid]];
+        int start = tid;
+        while (start > 0 && rs.ids[rs.perm[start - 1]] == e) --start;
+        flag = ((tid - start) % kVecTok) == 0;
+        a.ws.perm[tid] = rs.perm[tid];
+    }
+    int inc = flag;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+    }
+    if (lane == 63) rs.tmp[wave] = inc;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) inc += rs.tmp[w];
+    if (flag) rs.gpos[inc - 1] = tid;
+    if (tid == 255) rs.ngroups = inc;
+    __syncthreads();
+    const int G = rs.ngroups;
+    for (int g = tid; g < G; g += 256) {
+        const int gs = rs.gpos[g], ge = g + 1 < G ? rs.gpos[g + 1] : P;
+        a.ws.groups[g] = make_int4(rs.ids[rs.perm[gs]], gs, ge - gs, 0);
+    }
+    const int ns = d.has_shared ? (d.T + kVecTok - 1) / kVecTok : 0;
+    for (int j = tid; j < ns; j += 256)
+        a.ws.groups[G + j] = make_int4(d.E, j * kVecTok, min(kVecTok, d.T - j * kVecTok), 0);
+    if (tid == 0) {
+        a.ws.ctl[kCtlGroups] = G + ns;
+        a.ws.offsets[d.E] = P;
+    }
+    for (int e = tid; e < d.E; e += 256) {
+        int c = 0, below = 0;
+        for (int p = 0; p < P; ++p) {
+            c += rs.ids[p] == e;
+            below += rs.ids[p] < e;
+        }
+        a.ws.counts[e] = c;
+        a.ws.offsets[e] = below;
+    }
+}
+
+// -------------------------------------------------------- down, one token
+// Rows of the output: each wave pass covers RPW rows (LPR lanes per row, the
+// routed format's geometry; the shared Q8 expert reuses it with more chunks
+// per lane).  Every selected expert's row is requested before h is staged.
+constexpr int kMaxSel = 9;  // top_k <= 8 plus the shared expert
+
+template <int F, int FMT, bool DUMP>
+__global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
+    constexpr int L = DefLpr<F, FMT>::v;
+    constexpr int RPW = 64 / L;
+    __shared__ VecSmem<F, kMaxSel> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Dims &d = a.d;
+    const int G = a.ws.ctl[kCtlGroups];  // k routed groups (ascending id), then the shared expert
+    const int nr = d.has_shared ? G - 1 : G;
+    const int seg = lane % L, r = (blockIdx.x * 4 + wave) * RPW + lane / L;
+    const int64_t mb = mat_bytes(FMT, d.H, F);
+    RowRegs<F, FMT, L> rr[kMaxSel - 1];
+    RowRegs<F, kFmtQ8, L> rsh;
+#pragma unroll
+    for (int i = 0; i < kMaxSel - 1; ++i)
+        if (i < nr) rr[i].load(a.wt.down + (int64_t)a.ws.groups[i].x * mb, d.H, r, seg);
+    if (d.has_shared) rsh.load(a.wt.sh_down, d.H, r, seg);
+    if (tid < G) {
+        const int4 grp = a.ws.groups[tid];
+        const bool shared = grp.x == d.E;
+        const int p = shared ? d.k : a.ws.perm[grp.y];
+        sm.pair[tid] = p;
+        sm.row[tid] = p;
+        sm.w[tid] = shared ? 1.0f : a.ws.w[p];
+    }
+    __syncthreads();
+    stage_rows<F, kMaxSel, false>(sm, a.ws.hq, a.ws.hd, nullptr, G);
+    __syncthreads();
+    if constexpr (FMT == kFmtQ2) {
+        subblock_sums(sm, G);
+        __syncthreads();
+    }
+    // Same arithmetic per expert as the batched down + combine: y = w * (sum
+    // over lanes), summed in ascending expert id, the shared expert last.
+    const bool dump_row = DUMP && (r % a.dump.stride == 0);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxSel - 1; ++i)
+        if (i < nr) {
+            int32_t *dd = dump_row ? a.dump.down_sums +
+                                         ((int64_t)sm.pair[i] * (d.H / a.dump.stride) + r / a.dump.stride) *
+                                             a.dump.pitch_dn
+                                   : nullptr;
+            const float y = group_sum<L>(lane_dot<F, L>(rr[i], sm.aq[i], sm.ad[i], sm.as16[i], seg, dd));
+            acc = __fadd_rn(acc, __fmul_rn(sm.w[i], y));
+        }
+    if (d.has_shared) {
+        int32_t *dd = dump_row ? a.dump.down_sums +
+                                     ((int64_t)sm.pair[nr] * (d.H / a.dump.stride) + r / a.dump.stride) *
+                                         a.dump.pitch_dn
+                               : nullptr;
+        const float y = group_sum<L>(lane_dot<F, L>(rsh, sm.aq[nr], sm.ad[nr], sm.as16[nr], seg, dd));
+        acc = __fadd_rn(acc, __fmul_rn(1.0f, y));
+    }
+    if (seg == 0) a.out[r] = acc;
+}
+
+// ------------------------------------------------------------- launchers
+template <int H, bool DUMP>
+static hipError_t front_h(const LayerArgs &a, hipStream_t s) {
+    const Dims &d = a.d;
+    const int nq = (d.T * (H / 32) + 255) / 256;
+    int n_lead = nq;
+    if (d.route == kRouteLearned) {
+        const int nl = H >= 256 ? d.T * d.E : (d.T * d.E + 3) / 4;
+        n_lead = nl > nq ? nl : nq;
+    }
+    if (n_lead > 4096) n_lead = 4096;
+    const int ns = d.has_shared ? (d.F / GuRows<H, kFmtQ8>::v) * ((d.T + kVecTok - 1) / kVecTok) : 0;
+    decode_front_kernel<H, DUMP><<<dim3(n_lead + ns), dim3(256), 0, s>>>(a, n_lead);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_front(const LayerArgs &a, bool dump, hipStream_t s) {
+    switch (a.d.H) {
+        case 128: return dump ? front_h<128, true>(a, s) : front_h<128, false>(a, s);
+        case 256: return dump ? front_h<256, true>(a, s) : front_h<256, false>(a, s);
+        case 512: return dump ? front_h<512, true>(a, s) : front_h<512, false>(a, s);
+        case 1024: return dump ? front_h<1024, true>(a, s) : front_h<1024, false>(a, s);
+        case 2048: return dump ? front_h<2048, true>(a, s) : front_h<2048, false>(a, s);
+        case 4096: return dump ? front_h<4096, true>(a, s) : front_h<4096, false>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s) {
+    decode_select_kernel<<<dim3(1), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int F, int FMT, bool DUMP>
+static hipError_t down1_h(const LayerArgs &a, hipStream_t s) {
+    constexpr int RPW = 64 / DefLpr<F, FMT>::v;
+    decode_down1_kernel<F, FMT, DUMP><<<dim3(a.d.H / (4 * RPW)), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int FMT, bool DUMP>
+static hipError_t down1_f(const LayerArgs &a, hipStream_t s) {
+    switch (a.d.F) {
+        case 128: if constexpr (FMT == kFmtQ8) return down1_h<128, FMT, DUMP>(a, s); return hipErrorInvalidValue;
+        case 256: if constexpr (FMT == kFmtQ8) return down1_h<256, FMT, DUMP>(a, s); return hipErrorInvalidValue;
+        case 512: return down1_h<512, FMT, DUMP>(a, s);
+        case 1024: return down1_h<1024, FMT, DUMP>(a, s);
+        case 2048: return down1_h<2048, FMT, DUMP>(a, s);
+        case 4096: return down1_h<4096, FMT, DUMP>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_down1(const LayerArgs &a, bool dump, hipStream_t s) {
+    if (a.d.fmt == kFmtQ8) return dump ? down1_f<kFmtQ8, true>(a, s) : down1_f<kFmtQ8, false>(a, s);
+    return dump ? down1_f<kFmtQ2, true>(a, s) : down1_f<kFmtQ2, false>(a, s);
+}
+
+}  // namespace qrmoe

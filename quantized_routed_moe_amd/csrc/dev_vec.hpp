@@ -1,0 +1,240 @@
+// Device helpers of the VALU expert kernels: lane geometry, weight-row
+// registers, int8 x int8 block dot products (v_dot4c_i32_i8) with the two
+// block scales, activation staging, SwiGLU and the h quantizer.
+#pragma once
+
+#include "common.hpp"
+
+namespace qrmoe {
+
+// LDS of one workgroup: quantized activations of up to NTOK tokens, their
+// block scales, (2-bit weights) their 16-subblock code sums, h of 32 rows.
+template <int K, int NTOK>
+struct VecSmem {
+    alignas(16) int8_t aq[NTOK][K];
+    float ad[NTOK][K / 32];
+    int32_t as16[NTOK][K / 16];
+    float h[NTOK][kVecRows];
+    int32_t pair[NTOK];
+    int32_t row[NTOK];
+    float w[NTOK];
+};
+
+// Default lanes per weight row: Q8 rows are cut in 16-byte chunks (half
+// blocks), Q2 rows in 64-weight pieces (16 code bytes, 4 subblocks).
+template <int K, int FMT>
+struct DefLpr {
+    static constexpr int v = FMT == kFmtQ8 ? (K / 16 < 64 ? K / 16 : 64) : (K / 64 < 64 ? K / 64 : 64);
+};
+
+template <int K, int FMT, int LPR = DefLpr<K, FMT>::v>
+struct Geo {
+    static constexpr int L = LPR;
+    static constexpr int J = FMT == kFmtQ8 ? K / (16 * LPR) : K / (64 * LPR);  // chunks per lane
+    static constexpr int RPW = 64 / LPR;                                       // rows per wave pass
+    static_assert(J >= 1 && LPR <= 64 && (FMT == kFmtQ8 || J == 1), "lane geometry");
+};
+
+// One lane's part of one weight row.  Q8: chunk j is 16 code bytes at
+// 16*(seg + LPR*j) with the fp16 scale of its 32-block.  Q2: 64 weights at
+// 64*seg: 16 code bytes, 4 scale/min bytes, and the superblock's d, dmin.
+template <int K, int FMT, int LPR>
+struct RowRegs;
+
+template <int K, int LPR>
+struct RowRegs<K, kFmtQ8, LPR> {
+    static constexpr int J = Geo<K, kFmtQ8, LPR>::J;
+    int4 c[J];
+    float s[J];
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, int64_t R, int64_t r, int seg) {
+        const int4 *codes = reinterpret_cast<const int4 *>(mat + r * K);
+        const uint16_t *sc = reinterpret_cast<const uint16_t *>(mat + R * K) + r * (K / 32);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            c[j] = load_stream16(codes + seg + LPR * j);
+            s[j] = f16_to_f32(sc[(seg + LPR * j) >> 1]);
+        }
+    }
+};
+
+template <int K, int LPR>
+struct RowRegs<K, kFmtQ2, LPR> {
+    int4 c;
+    uint32_t sm;
+    float d, dmin;
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, int64_t R, int64_t r, int seg) {
+        c = load_stream16(reinterpret_cast<const int4 *>(mat + r * (K / 4)) + seg);
+        sm = *reinterpret_cast<const uint32_t *>(mat + R * K / 4 + r * (K / 16) + 4 * seg);
+        const uint32_t dd =
+            *reinterpret_cast<const uint32_t *>(mat + R * K / 4 + R * K / 16 + (r * (K / 256) + seg / 4) * 4);
+        d = f16_to_f32((uint16_t)(dd & 0xffff));
+        dmin = f16_to_f32((uint16_t)(dd >> 16));
+    }
+};
+
+// Partial dot of one lane's part of a row with a quantized activation row
+// (floating-point steps written with explicit rounding intrinsics so that
+// every kernel inlining this computes bit-identical partials)
+// (aq: K int8 codes, ad: K/32 scales, as16: K/16 subblock code sums, all in
+// LDS).  With dump != nullptr the exact int32 block sums are written: per
+// 32-block (Q8; the two halves of a block sit in lanes seg, seg^1) or per
+// 16-weight subblock (Q2).
+template <int K, int LPR>
+__device__ __forceinline__ float lane_dot(const RowRegs<K, kFmtQ8, LPR> &w, const int8_t *aq, const float *ad,
+                                          const int32_t *, int seg, int32_t *dump) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Geo<K, kFmtQ8, LPR>::J; ++j) {
+        const int chunk = seg + LPR * j;
+        const int4 x = *reinterpret_cast<const int4 *>(aq + chunk * 16);
+        int I = sdot4(w.c[j].x, x.x, 0);
+        I = sdot4(w.c[j].y, x.y, I);
+        I = sdot4(w.c[j].z, x.z, I);
+        I = sdot4(w.c[j].w, x.w, I);
+        acc = __fmaf_rn((float)I, __fmul_rn(w.s[j], ad[chunk >> 1]), acc);
+        if (dump) {
+            const int full = I + __shfl_xor(I, 1);
+            if ((seg & 1) == 0) dump[chunk >> 1] = full;
+        }
+    }
+    return acc;
+}
+
+template <int K, int LPR>
+__device__ __forceinline__ float lane_dot(const RowRegs<K, kFmtQ2, LPR> &w, const int8_t *aq, const float *ad,
+                                          const int32_t *as16, int seg, int32_t *dump) {
+    const int4 *xp = reinterpret_cast<const int4 *>(aq + 64 * seg);
+    const int words[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+    int SP[2] = {0, 0}, SM[2] = {0, 0};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int4 x = xp[jj];
+        const uint32_t wv = (uint32_t)words[jj];
+        int P = sdot4((int)(wv & 0x03030303u), x.x, 0);
+        P = sdot4((int)((wv >> 2) & 0x03030303u), x.y, P);
+        P = sdot4((int)((wv >> 4) & 0x03030303u), x.z, P);
+        P = sdot4((int)((wv >> 6) & 0x03030303u), x.w, P);
+        const int s = (int)((w.sm >> (8 * jj)) & 15u), m = (int)((w.sm >> (8 * jj + 4)) & 15u);
+        SP[jj >> 1] += s * P;
+        SM[jj >> 1] += m * as16[4 * seg + jj];
+        if (dump) dump[4 * seg + jj] = P;
+    }
+    // explicit roundings: the same value in every kernel that inlines this
+    const float b0 = __fsub_rn(__fmul_rn(w.d, (float)SP[0]), __fmul_rn(w.dmin, (float)SM[0]));
+    const float b1 = __fsub_rn(__fmul_rn(w.d, (float)SP[1]), __fmul_rn(w.dmin, (float)SM[1]));
+    return __fadd_rn(__fmul_rn(ad[2 * seg], b0), __fmul_rn(ad[2 * seg + 1], b1));
+}
+
+// Copy the quantized rows `rows[0..cnt)` of (q, dq, s16) into LDS slots 0..cnt.
+template <int K, int NTOK, bool S16>
+__device__ __forceinline__ void stage_rows(VecSmem<K, NTOK> &sm, const int8_t *__restrict__ q,
+                                           const float *__restrict__ dq, const int32_t *__restrict__ s16, int cnt) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < cnt * (K / 16); i += 256) {
+        const int tok = i / (K / 16), c = i % (K / 16);
+        reinterpret_cast<int4 *>(sm.aq[tok])[c] = reinterpret_cast<const int4 *>(q + (int64_t)sm.row[tok] * K)[c];
+    }
+    for (int i = tid; i < cnt * (K / 32); i += 256) {
+        const int tok = i / (K / 32), b = i % (K / 32);
+        sm.ad[tok][b] = dq[(int64_t)sm.row[tok] * (K / 32) + b];
+    }
+    if constexpr (S16) {
+        for (int i = tid; i < cnt * (K / 16); i += 256) {
+            const int tok = i / (K / 16), g = i % (K / 16);
+            sm.as16[tok][g] = s16[(int64_t)sm.row[tok] * (K / 16) + g];
+        }
+    }
+}
+
+// Sums of the staged codes over 16-subblocks (for 2-bit weights applied to h).
+template <int K, int NTOK>
+__device__ __forceinline__ void subblock_sums(VecSmem<K, NTOK> &sm, int cnt) {
+    for (int i = threadIdx.x; i < cnt * (K / 16); i += 256) {
+        const int tok = i / (K / 16), g = i % (K / 16);
+        const int4 v = reinterpret_cast<const int4 *>(sm.aq[tok])[g];
+        int s = sdot4(v.x, 0x01010101, 0);
+        s = sdot4(v.y, 0x01010101, s);
+        s = sdot4(v.z, 0x01010101, s);
+        s = sdot4(v.w, 0x01010101, s);
+        sm.as16[tok][g] = s;
+    }
+}
+
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Rows per workgroup of the gate/up kernels that leave h unquantized: at least
+// 8 (small workgroups spread a 2048-row matrix over 256 of them) and a whole
+// wave pass of each of the 4 waves.
+template <int K, int FMT>
+struct GuRows {
+    static constexpr int v = 4 * Geo<K, FMT>::RPW > 8 ? 4 * Geo<K, FMT>::RPW : 8;
+};
+
+// Gate/up of one expert for rows r0..r0+ROWS-1 and the cnt staged tokens,
+// then SwiGLU.  QUANT: quantize the 32-row h block of every token here
+// (ROWS == 32) into hq/hd; otherwise store h in fp32 for the consumer to
+// quantize (the same values give the same codes wherever they are
+// quantized).  sm.pair[] names the output pair of each token.
+template <int K, int FMT, int NTOK, int ROWS, bool QUANT, bool DUMP>
+__device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint8_t *__restrict__ gmat,
+                            const uint8_t *__restrict__ umat, int cnt, int r0) {
+    using G = Geo<K, FMT>;
+    constexpr int PASSES = ROWS / (4 * G::RPW);
+    static_assert(PASSES >= 1 && ROWS % (4 * G::RPW) == 0 && (!QUANT || ROWS == kVecRows), "row geometry");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Dims &d = a.d;
+    const int seg = lane % G::L, rsub = lane / G::L;
+    RowRegs<K, FMT, G::L> wg, wu;
+    int row_local = wave * G::RPW + rsub;
+    wg.load(gmat, d.F, r0 + row_local, seg);
+    wu.load(umat, d.F, r0 + row_local, seg);
+#pragma unroll 1
+    for (int pass = 0; pass < PASSES; ++pass) {
+        RowRegs<K, FMT, G::L> ng, nu;
+        const int next_local = ((pass + 1) * 4 + wave) * G::RPW + rsub;
+        if (pass + 1 < PASSES) {
+            ng.load(gmat, d.F, r0 + next_local, seg);
+            nu.load(umat, d.F, r0 + next_local, seg);
+        }
+        const int r = r0 + row_local;
+        const bool dump_row = DUMP && (r % a.dump.stride == 0);
+        for (int tok = 0; tok < cnt; ++tok) {
+            int32_t *dg = nullptr, *du = nullptr;
+            if (dump_row) {
+                const int64_t base =
+                    ((int64_t)sm.pair[tok] * (d.F / a.dump.stride) + r / a.dump.stride) * a.dump.pitch_gu;
+                dg = a.dump.gate_sums + base;
+                du = a.dump.up_sums + base;
+            }
+            const float gp = group_sum<G::L>(lane_dot<K, G::L>(wg, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dg));
+            const float up = group_sum<G::L>(lane_dot<K, G::L>(wu, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, du));
+            if (seg == 0) {
+                const float hv = swiglu(gp, up);
+                if constexpr (QUANT)
+                    sm.h[tok][row_local] = hv;
+                else
+                    a.ws.h[(int64_t)sm.pair[tok] * d.F + r] = hv;
+            }
+        }
+        if (pass + 1 < PASSES) {
+            wg = ng;
+            wu = nu;
+            row_local = next_local;
+        }
+    }
+    if constexpr (QUANT) {
+        __syncthreads();
+        const int tok = tid >> 5, i = tid & 31;
+        const float v = tok < cnt ? sm.h[tok][i] : 0.0f;
+        const float amax = group_max<32>(fabsf(v));
+        if (tok < cnt) {
+            const float dsc = quant_scale(amax);
+            const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
+            const int p = sm.pair[tok];
+            a.ws.hq[(int64_t)p * d.F + r0 + i] = (int8_t)quant_code(v, inv);
+            if (i == 0) a.ws.hd[(int64_t)p * (d.F / 32) + r0 / 32] = dsc;
+        }
+    }
+}
+
+}  // namespace qrmoe

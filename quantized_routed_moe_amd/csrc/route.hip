@@ -17,206 +17,9 @@
 //  - Stable sort of the (token, slot) pairs by expert and the per-expert
 //    work lists the expert kernels consume ("ds4: dfm Edition": per-expert
 //    worklists, expert-major schedule).
-#include <climits>
-#include <cmath>
-
-#include "common.hpp"
+#include "dev_route.hpp"
 
 namespace qrmoe {
-
-// ------------------------------------------------------------ quantizer
-// One thread quantizes one 32-block of a row of H floats.
-__device__ __forceinline__ void quant_one_block(const float *__restrict__ x, int8_t *__restrict__ xq,
-                                                float *__restrict__ xd, int32_t *__restrict__ xs16, int64_t blk) {
-    const float4 *src = reinterpret_cast<const float4 *>(x + blk * 32);
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float4 f = src[i];
-        v[4 * i] = f.x;
-        v[4 * i + 1] = f.y;
-        v[4 * i + 2] = f.z;
-        v[4 * i + 3] = f.w;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const float d = quant_scale(amax);
-    const float inv = d > 0.0f ? 1.0f / d : 0.0f;
-    uint32_t words[8];
-    int s0 = 0, s1 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t wv = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            int q = quant_code(v[4 * i + c], inv);
-            if (i < 4) s0 += q; else s1 += q;
-            wv |= ((uint32_t)q & 0xffu) << (8 * c);
-        }
-        words[i] = wv;
-    }
-    uint4 *dst = reinterpret_cast<uint4 *>(xq + blk * 32);
-    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
-    xd[blk] = d;
-    if (xs16) {
-        xs16[2 * blk] = s0;
-        xs16[2 * blk + 1] = s1;
-    }
-}
-
-// --------------------------------------------------------- router logits
-// Pairwise fp64 tree of n = N products held in registers.  Level 1 may be
-// contracted to fma(a1, b1, a0*b0): both products are exact in fp64, so the
-// fused and unfused forms round identically.
-template <int N>
-__device__ __forceinline__ double prod_tree(const float *a, const float *b) {
-    if constexpr (N == 1) {
-        return (double)a[0] * (double)b[0];
-    } else {
-        return prod_tree<N / 2>(a, b) + prod_tree<N / 2>(a + N / 2, b + N / 2);
-    }
-}
-
-template <int N>
-__device__ __forceinline__ double dtree(const double *v) {
-    if constexpr (N == 1) {
-        return v[0];
-    } else {
-        return dtree<N / 2>(v) + dtree<N / 2>(v + N / 2);
-    }
-}
-
-// Pairwise sum over one lane's aligned segment of SEG elements.
-template <int SEG>
-__device__ __forceinline__ double segment_tree(const float *__restrict__ xa, const float *__restrict__ wa) {
-    constexpr int CH = SEG < 16 ? SEG : 16;
-    constexpr int NC = SEG / CH;
-    double part[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        float xv[CH], wv[CH];
-        if constexpr (CH % 4 == 0) {
-#pragma unroll
-            for (int i = 0; i < CH / 4; ++i) {
-                float4 a = reinterpret_cast<const float4 *>(xa + c * CH)[i];
-                float4 b = reinterpret_cast<const float4 *>(wa + c * CH)[i];
-                xv[4 * i] = a.x; xv[4 * i + 1] = a.y; xv[4 * i + 2] = a.z; xv[4 * i + 3] = a.w;
-                wv[4 * i] = b.x; wv[4 * i + 1] = b.y; wv[4 * i + 2] = b.z; wv[4 * i + 3] = b.w;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                xv[i] = xa[c * CH + i];
-                wv[i] = wa[c * CH + i];
-            }
-        }
-        part[c] = prod_tree<CH>(xv, wv);
-    }
-    return dtree<NC>(part);
-}
-
-// One wave computes one logit: lane l owns elements [l*SEG, (l+1)*SEG); the
-// segment sums are combined by an xor butterfly whose pairing (1, 2, 4, ...)
-// is the upper part of the same adjacent-pair tree.
-template <int H>
-__device__ __forceinline__ float wave_logit(const float *__restrict__ xrow, const float *__restrict__ wrow, int lane) {
-    constexpr int SEG = H / 64;
-    double v = segment_tree<SEG>(xrow + lane * SEG, wrow + lane * SEG);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    return (float)v;
-}
-
-// ------------------------------------------------------------- selection
-__device__ __forceinline__ float score_of(float l) { return (float)(1.0 / (1.0 + exp(-(double)l))); }
-
-// One wave selects the top-k experts of one token.
-__device__ void select_learned_wave(const float *__restrict__ lrow, const float *__restrict__ bias, int E, int k,
-                                    int32_t *ids_out, float *w_out, int lane) {
-    constexpr int MAXPER = 16;  // E <= 1024
-    const int per = (E + 63) / 64;
-    float key[MAXPER], sc[MAXPER];
-#pragma unroll
-    for (int i = 0; i < MAXPER; ++i) {
-        key[i] = -INFINITY;
-        sc[i] = 0.0f;
-        const int e = lane + 64 * i;
-        if (i < per && e < E) {
-            sc[i] = score_of(lrow[e]);
-            key[i] = sc[i] + (bias ? bias[e] : 0.0f);
-        }
-    }
-    int sel_e[8];
-    float sel_s[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        sel_e[j] = 0;
-        sel_s[j] = 0.0f;
-        if (j < k) {
-            float bk = -INFINITY;
-            int be = INT_MAX;
-#pragma unroll
-            for (int i = 0; i < MAXPER; ++i) {
-                const int e = lane + 64 * i;
-                if (i < per && e < E && (key[i] > bk || (key[i] == bk && e < be))) {
-                    bk = key[i];
-                    be = e;
-                }
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                float ok = __shfl_xor(bk, o);
-                int oe = __shfl_xor(be, o);
-                if (ok > bk || (ok == bk && oe < be)) {
-                    bk = ok;
-                    be = oe;
-                }
-            }
-            const int owner = be & 63, slot = be >> 6;
-            float mine = 0.0f;
-#pragma unroll
-            for (int i = 0; i < MAXPER; ++i)
-                if (i == slot) {
-                    mine = sc[i];
-                    if (lane == owner) key[i] = -INFINITY;
-                }
-            sel_s[j] = __shfl(mine, owner);
-            sel_e[j] = be;
-        }
-    }
-    float S = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < k) S += sel_s[j];
-    if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < k) {
-                ids_out[j] = sel_e[j];
-                w_out[j] = sel_s[j] / S;
-            }
-    }
-}
-
-__device__ void select_hash_wave(const int32_t *__restrict__ token_ids, const int32_t *__restrict__ table, int t,
-                                 int vocab, int E, int k, int32_t *ids_out, float *w_out, int32_t *flags, int lane) {
-    int id = token_ids[t];
-    if (id < 0 || id >= vocab) {
-        if (lane == 0) atomicOr(flags, 1);
-        id = 0;
-    }
-    if (lane < k) {
-        int e = table[(int64_t)id * k + lane];
-        if (e < 0 || e >= E) {
-            atomicOr(flags, 2);
-            e = 0;
-        }
-        ids_out[lane] = e;
-        w_out[lane] = 1.0f / (float)k;
-    }
-}
 
 // ------------------------------------------------- sort + work-list build
 // Runs in ONE workgroup of 256 threads.  Stable counting sort of the P = T*k
@@ -294,75 +97,6 @@ __device__ void sort_and_group(const Dims &d, const Ws &ws, int G, SortSmem &sm)
     for (int j = tid; j < shared_groups; j += 256)
         ws.groups[routed_groups + j] = make_int4(E, j * G, min(G, d.T - j * G), 0);
     if (tid == 0) ws.ctl[kCtlGroups] = routed_groups + shared_groups;
-}
-
-// ------------------------------------------------------ decode routing
-// Kernel 1 (many workgroups): quantize x; learned layers also compute the
-// T*E logits, one wave per logit.  Kernel 2 (one workgroup): select, sort,
-// build the work list.  The kernel boundary orders the two; no device-scope
-// fences are used (on this multi-XCD part they write back and invalidate L2).
-template <int H>
-__global__ __launch_bounds__(256) void route_logits_kernel(LayerArgs a) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const Dims &d = a.d;
-    const int nblk = d.T * (H / 32);
-    for (int b = blockIdx.x * 256 + tid; b < nblk; b += gridDim.x * 256)
-        quant_one_block(a.x, a.ws.xq, a.ws.xd, d.fmt == kFmtQ2 ? a.ws.xs16 : nullptr, b);
-    if (d.route == kRouteLearned) {
-        const int nlog = d.T * d.E;
-        for (int le = blockIdx.x * 4 + wave; le < nlog; le += gridDim.x * 4) {
-            const int t = le / d.E, e = le % d.E;
-            float l = wave_logit<H>(a.x + (int64_t)t * H, a.wt.router_w + (int64_t)e * H, lane);
-            if (lane == 0) a.ws.logits[le] = l;
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void select_sort_kernel(LayerArgs a) {
-    __shared__ SortSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const Dims &d = a.d;
-    for (int t = wave; t < d.T; t += 4) {
-        if (d.route == kRouteLearned)
-            select_learned_wave(a.ws.logits + (int64_t)t * d.E, a.wt.router_b, d.E, d.k, a.ws.ids + t * d.k,
-                                a.ws.w + t * d.k, lane);
-        else
-            select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.E, d.k, a.ws.ids + t * d.k, a.ws.w + t * d.k,
-                             a.ws.ctl + kCtlFlags, lane);
-    }
-    __syncthreads();
-    sort_and_group(d, a.ws, a.group_tok, sm);
-}
-
-template <int H>
-static hipError_t launch_route_logits_h(const LayerArgs &a, hipStream_t s) {
-    const int work_waves = a.d.route == kRouteLearned ? a.d.T * a.d.E : 0;
-    int blocks = (work_waves + 3) / 4;
-    const int qblocks = (a.d.T * (H / 32) + 255) / 256;
-    if (blocks < qblocks) blocks = qblocks;
-    if (blocks > 2048) blocks = 2048;
-    if (blocks < 1) blocks = 1;
-    route_logits_kernel<H><<<dim3(blocks), dim3(256), 0, s>>>(a);
-    return hipGetLastError();
-}
-
-hipError_t launch_route_decode(const LayerArgs &a, hipStream_t s) {
-    hipError_t err;
-    switch (a.d.H) {
-        case 128: err = launch_route_logits_h<128>(a, s); break;
-        case 256: err = launch_route_logits_h<256>(a, s); break;
-        case 512: err = launch_route_logits_h<512>(a, s); break;
-        case 1024: err = launch_route_logits_h<1024>(a, s); break;
-        case 2048: err = launch_route_logits_h<2048>(a, s); break;
-        case 4096: err = launch_route_logits_h<4096>(a, s); break;
-        default: return hipErrorInvalidValue;
-    }
-    return err;
-}
-
-hipError_t launch_select_sort(const LayerArgs &a, hipStream_t s) {
-    select_sort_kernel<<<dim3(1), dim3(256), 0, s>>>(a);
-    return hipGetLastError();
 }
 
 // --------------------------------------------------- batched (large T)
@@ -478,7 +212,12 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(LayerArgs a) {
 #pragma unroll
         for (int ei = 0; ei < 2; ++ei) {
             const int t = tb + tl + 16 * ti, e = eb + el + 16 * ei;
-            if (t < a.d.T && e < a.d.E) a.ws.logits[(int64_t)t * a.d.E + e] = (float)r[ti * 2 + ei];
+            if (t < a.d.T && e < a.d.E) {
+                const int64_t i = (int64_t)t * a.d.E + e;
+                const float l = (float)r[ti * 2 + ei];
+                a.ws.logits[i] = l;
+                score_key(l, a.wt.router_b, e, a.ws.scores + i, a.ws.keys + i);
+            }
         }
 }
 
@@ -489,17 +228,21 @@ hipError_t launch_logits(const LayerArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+__device__ __forceinline__ void select_token(const LayerArgs &a, int t, int32_t *ids, float *w, int lane) {
+    const Dims &d = a.d;
+    if (d.route == kRouteLearned)
+        select_keys_wave(a.ws.keys + (int64_t)t * d.E, a.ws.scores + (int64_t)t * d.E, d.E, d.k, ids, w, lane);
+    else
+        select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.E, d.k, ids, w, a.ws.ctl + kCtlFlags, lane);
+}
+
 __global__ __launch_bounds__(256) void select_kernel(LayerArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.d.T) return;
-    if (a.d.route == kRouteLearned)
-        select_learned_wave(a.ws.logits + (int64_t)t * a.d.E, a.wt.router_b, a.d.E, a.d.k, a.ws.ids + t * a.d.k,
-                            a.ws.w + t * a.d.k, lane);
-    else
-        select_hash_wave(a.token_ids, a.wt.table, t, a.d.vocab, a.d.E, a.d.k, a.ws.ids + t * a.d.k, a.ws.w + t * a.d.k,
-                         a.ws.ctl + kCtlFlags, lane);
+    select_token(a, t, a.ws.ids + t * a.d.k, a.ws.w + t * a.d.k, lane);
 }
+
 
 hipError_t launch_select(const LayerArgs &a, hipStream_t s) {
     select_kernel<<<dim3((a.d.T + 3) / 4), dim3(256), 0, s>>>(a);

@@ -196,8 +196,11 @@ def test_empty_batch_is_a_no_op():
 
 # ------------------------------------------------ determinism / batching
 @pytest.mark.parametrize("cfg", [ms.LayerConfig("batch_learned", 512, 32, 4, 256, 12, seed=31),
+                                 ms.LayerConfig("batch_learned_T3", 1024, 64, 6, 512, 3, seed=36),
                                  ms.LayerConfig("batch_hash", 512, 32, 4, 256, 12, route="hash", vocab=300,
-                                                seed=32)], ids=lambda c: c.name)
+                                                seed=32),
+                                 ms.LayerConfig("batch_q2_T40", 512, 32, 4, 512, 40, routed_fmt="q2", seed=35)],
+                         ids=lambda c: c.name)
 def test_batched_equals_single_token_calls_bitwise(cfg):
     inp, layer = case(cfg)
     x = torch.from_numpy(inp["x"]).cuda()
@@ -254,3 +257,31 @@ def test_full_size_prefill_sampled():
     rows = np.r_[0, 1, 2, 511, 1024, 1500, 2046, 2047, np.arange(37, 2048, 173)]
     check(cfg, inp, g, rows=np.unique(rows), stride=128)
     assert np.count_nonzero(g["counts"]) > 0
+
+
+# ------------------------------------------------------- graph replay
+@pytest.mark.parametrize("cfg", [ms.LayerConfig("graph_T1", 512, 32, 4, 256, 1, seed=41),
+                                 ms.LayerConfig("graph_T7_hash", 512, 32, 4, 256, 7, route="hash", vocab=99, seed=42),
+                                 ms.LayerConfig("graph_T40", 512, 32, 4, 256, 40, seed=43)], ids=lambda c: c.name)
+def test_graph_replay_matches_eager(cfg):
+    """The layer captured in a HIP graph replays to the eager result, replay after replay,
+    with eager work and synchronisations in between (nothing in the path is a memset node)."""
+    qr = _qr()
+    inp, layer = case(cfg)
+    x = torch.from_numpy(inp["x"]).cuda()
+    tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route == "hash" else None
+    want = layer.forward(x, tok).clone()
+    out = torch.empty_like(want)
+    layer.ensure_workspace(cfg.tokens)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qr.layer_forward(layer.shape, layer.weights(), x, tok, out, layer.ws, torch.cuda.current_stream())
+    for i in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), want.view(torch.int32)), f"replay {i} differs"
+        other = layer.forward(x, tok)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int32), want.view(torch.int32))
