@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libqrmoe.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "pack.hip", "route.hip", "expert_vec.hip", "decode.hip"]
+SOURCES = ["api.cpp", "pack.hip", "route.hip", "expert_vec.hip", "decode.hip", "expert_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -ffp-contract=off: floating-point operations round exactly as written (fused
 # multiply-adds only where the source asks for one), so every kernel that

@@ -14,7 +14,7 @@ using namespace qrmoe;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMfmaTile = 64;  // tokens per MFMA work tile
+constexpr int kMfmaTile = 64;  // pairs per MFMA work tile
 
 inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -189,12 +189,22 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
             run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
         }
     } else {
+        // Q8 experts go through the grouped int8 MFMA GEMMs (32-pair tiles);
+        // 2-bit experts and the smallest shapes stay on the VALU kernels.
+        const bool mfma = shape->routed_fmt == MOE_FMT_Q8_32 && H >= 256 && shape->ffn >= 256;
+        const int64_t tiles = mfma ? max_groups(shape, T, kMfmaTile) : mg;
+        a.group_tok = mfma ? kMfmaTile : kVecTok;
         run(MOE_STAGE_QUANT, [&] { return launch_quant(a, s); });
         if (learned) run(MOE_STAGE_LOGITS, [&] { return launch_logits(a, s); });
         run(MOE_STAGE_SELECT, [&] { return launch_select(a, s); });
         run(MOE_STAGE_SORT, [&] { return launch_sort(a, s); });
-        run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, false, dump, s); });
-        run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
+        if (mfma) {
+            run(MOE_STAGE_GATEUP, [&] { return launch_gateup_mfma(a, (int)tiles, dump, s); });
+            run(MOE_STAGE_DOWN, [&] { return launch_down_mfma(a, (int)tiles, dump, s); });
+        } else {
+            run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, false, dump, s); });
+            run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
+        }
         run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
     }
     if (err == hipSuccess && dbg) {

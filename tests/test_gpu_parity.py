@@ -147,6 +147,9 @@ SMALL = [
     ms.LayerConfig("q8_all_experts", 256, 8, 8, 128, 6, seed=20),
     ms.LayerConfig("q8_nobias_T1", 1024, 64, 6, 512, 1, bias=False, seed=21),
     ms.LayerConfig("q2_hash_T32", 512, 16, 6, 512, 32, routed_fmt="q2", route="hash", vocab=64, seed=22),
+    ms.LayerConfig("q8_mfma_1024_T300", 1024, 16, 4, 512, 300, seed=26),
+    ms.LayerConfig("q8_mfma_hash_T77", 512, 64, 6, 256, 77, route="hash", vocab=5000, seed=27),
+    ms.LayerConfig("q8_mfma_noshared_T45", 256, 8, 3, 256, 45, shared=False, seed=28),
 ]
 
 
@@ -174,6 +177,17 @@ def test_skewed_bias_sends_all_tokens_to_one_expert():
     g = run_gpu(cfg, inp, layer, stride=2)
     assert g["counts"][5] == 64
     check(cfg, inp, g, stride=2, name="skew")
+
+
+def test_skewed_bias_mfma_tiles():
+    """One expert takes every token: 200 pairs cut into seven 32-pair MFMA tiles (last one ragged)."""
+    cfg = ms.LayerConfig("skew_mfma", 512, 16, 2, 256, 200, seed=29)
+    inp = ms.make_inputs(cfg)
+    inp["router_b"][3] = 10.0
+    layer = _qr().MoELayer(512, 16, 2, 256).load(inp)
+    g = run_gpu(cfg, inp, layer, stride=4)
+    assert g["counts"][3] == 200
+    check(cfg, inp, g, stride=4, name="skew_mfma")
 
 
 def test_max_tokens_small_shape():
