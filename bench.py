@@ -11,8 +11,9 @@ Timing: W eager warm-up steps, then the K timed steps are replayed from a
 captured HIP graph (per-call host overhead excluded, as in a captured decode
 loop); every step uses a different token and one of R address-distinct copies
 of the weights every step re-reads (router, shared expert), so the 256 MB
-Infinity Cache cannot serve them across steps.  A second, eager pass with
-HIP events around each kernel gives the per-kernel durations used for the
+Infinity Cache cannot serve them across steps.  A second, eager pass takes
+each kernel's start and end from HIP events recorded by its own launch
+(hipExtLaunchKernelGGL), the per-kernel durations used for the
 roofline entry.  The CPU oracle is then timed on a bounded sample of the same
 workload on the host cores.
 """
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("PMC_FETCH", "PMC_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/traffic.txt for --config from rocprofv3 --pmc CSVs and exit")
     return ap.parse_args()
 
 
@@ -57,6 +60,189 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "copies": 5}))
 
 
+# --------------------------------------------------------------- accounting
+# Kernel sources per stage kernel: a stored byte count applies only while
+# these files (and the build flags) are unchanged.
+CSRC = os.path.join(ROOT, "quantized_routed_moe_amd", "csrc")
+KERNEL_SOURCES = {
+    "decode_front_kernel": ["decode.hip", "dev_route.hpp", "dev_vec.hpp", "common.hpp"],
+    "decode_select_kernel": ["decode.hip", "dev_route.hpp", "dev_vec.hpp", "common.hpp"],
+    "decode_down1_kernel": ["decode.hip", "dev_route.hpp", "dev_vec.hpp", "common.hpp"],
+    "gateup_vec_kernel": ["expert_vec.hip", "dev_vec.hpp", "common.hpp"],
+    "down_vec_kernel": ["expert_vec.hip", "dev_vec.hpp", "common.hpp"],
+    "combine_kernel": ["expert_vec.hip", "dev_vec.hpp", "common.hpp"],
+    "gateup_mfma_kernel": ["expert_mfma.hip", "dev_vec.hpp", "common.hpp"],
+    "down_mfma_kernel": ["expert_mfma.hip", "dev_vec.hpp", "common.hpp"],
+    "quant_kernel": ["route.hip", "dev_route.hpp", "common.hpp"],
+    "logits_tiled_kernel": ["route.hip", "dev_route.hpp", "common.hpp"],
+    "select_kernel": ["route.hip", "dev_route.hpp", "common.hpp"],
+    "sort_kernel": ["route.hip", "dev_route.hpp", "common.hpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+
+
+def kernel_base(name):
+    """'void qrmoe::gateup_vec_kernel<4096, 1, false, true>(...)' -> 'gateup_vec_kernel'."""
+    import re
+    m = re.search(r"qrmoe::(\w+)", name)
+    return m.group(1) if m else None
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "quantized_routed_moe_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stage_kernel(cfg, stage):
+    """Name of the one kernel a stage launches on this workload's path."""
+    T, mfma = cfg.tokens, (cfg.routed_fmt == "q8" and cfg.hidden >= 256 and cfg.ffn >= 256)
+    if T <= 32:
+        return {"route": "decode_front_kernel", "select": "decode_select_kernel", "gateup": "gateup_vec_kernel",
+                "down": "decode_down1_kernel" if T == 1 else "down_vec_kernel",
+                "combine": "combine_kernel"}.get(stage)
+    return {"quant": "quant_kernel", "logits": "logits_tiled_kernel", "select": "select_kernel",
+            "sort": "sort_kernel", "gateup": "gateup_mfma_kernel" if mfma else "gateup_vec_kernel",
+            "down": "down_mfma_kernel" if mfma else "down_vec_kernel", "combine": "combine_kernel"}.get(stage)
+
+
+def u_avg_of(used, warmup, G, K):
+    return sum(used[warmup + i % G] for i in range(K)) / K
+
+
+def stage_model(cfg, qr, u_avg):
+    """Algorithmic bytes (and int8 MFMA operations) per launch of each stage.
+
+    Bytes count what a stage must move at least once: the weights of every
+    expert that receives a token, router weights, activations read and
+    results written (x fp32, int8 codes + fp32 block scales, fp32 h, fp32
+    y, fp32 out).  u_avg is the mean number of distinct routed experts per
+    step.  Ops count 2 per int8 multiply-add of the expert GEMMs."""
+    T, H, E, k, F = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn
+    fmt = qr.FMT[cfg.routed_fmt]
+    sh = 1 if cfg.shared else 0
+    learned = cfg.route == "learned"
+    mq8_gu, mq8_dn = qr.matrix_bytes(qr.FMT_Q8, F, H), qr.matrix_bytes(qr.FMT_Q8, H, F)
+    mr_gu, mr_dn = qr.matrix_bytes(fmt, F, H), qr.matrix_bytes(fmt, H, F)
+    Pr, P = T * k, T * k + sh * T
+    x32 = T * H * 4
+    xq = T * H + T * (H // 32) * 4
+    hq = lambda n: n * F + n * (F // 32) * 4
+    router = E * H * 4 if learned else T * k * 4
+    rout = 3 * T * E * 4 if learned else 0
+    st = {}
+    if T <= 32:
+        st["route"] = router + x32 + xq + rout + sh * (2 * mq8_gu + T * F * 4)
+        st["select"] = (2 * T * E * 4 if learned else T * 4) + sh * (T * F * 4 + hq(T)) + T * k * 12
+        st["gateup"] = u_avg * 2 * mr_gu + xq + hq(Pr)
+        if T == 1:
+            st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + x32
+        else:
+            st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + P * H * 4
+            st["combine"] = P * H * 4 + x32
+    else:
+        st["quant"] = x32 + xq
+        if learned:
+            st["logits"] = router + x32 + rout
+        st["select"] = (2 * T * E * 4 if learned else T * 4) + T * k * 8
+        st["sort"] = T * k * 4 * 3
+        st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P)
+        st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + P * H * 4
+        st["combine"] = P * H * 4 + x32
+    ops = {"gateup": 2 * P * 2 * F * H, "down": 2 * P * H * F}
+    layer = (u_avg * (2 * mr_gu + mr_dn) + sh * (2 * mq8_gu + mq8_dn) + (router if learned else 0) + 2 * x32)
+    return {"stages": {s: {"bytes": b, "ops": ops.get(s)} for s, b in st.items()}, "layer_bytes": layer}
+
+
+def stored_traffic(cfg, kernel):
+    """HBM bytes per launch from profiles/traffic.txt, or None when absent or
+    when the kernel's sources changed after the counters were taken."""
+    if not kernel or not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = source_hash(kernel)
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) < 3 or line.startswith("#") or f[0] != cfg.name or f[1] != kernel:
+            continue
+        kv = dict(x.split("=", 1) for x in f[2:])
+        if kv.get("src") != want:
+            return None
+        return float(kv["bytes"])
+    return None
+
+
+def make_roofline(cfg, model, dom, dom_us):
+    kern = stage_kernel(cfg, dom)
+    st = model["stages"].get(dom, {})
+    traffic = stored_traffic(cfg, kern)
+    if kern in ("gateup_mfma_kernel", "down_mfma_kernel"):
+        ops = st["ops"]
+        ach = ops / (dom_us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic, "kernel": kern, "stage": dom,
+                "avg_launch_us": round(dom_us, 3), "algorithmic_ops_per_launch": int(ops),
+                "algorithmic_bytes_per_launch": int(st["bytes"])}
+    b = st.get("bytes")
+    ach = b / (dom_us * 1e-6) / 1e9 if b else None
+    return {"bound": "hbm", "achieved": round(ach, 1) if b else None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4) if b else None, "traffic": traffic, "kernel": kern, "stage": dom,
+            "avg_launch_us": round(dom_us, 3), "algorithmic_bytes_per_launch": int(b) if b else None}
+
+
+def traffic_from(args):
+    """Writes profiles/traffic.txt lines for one workload from rocprofv3 --pmc
+    CSVs: FETCH_SIZE and WRITE_SIZE of the layer kernels (KiB per dispatch)
+    and of a plain 1 GiB device copy, which scales each counter to bytes."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        d = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return d
+
+    copy_bytes = 1 << 30
+
+    def copy_factor(path, counter):
+        v = [x for n, xs in per_kernel(path, counter).items() if "copyBuffer" in n or "copy" in n for x in xs]
+        v = [x for x in v if x * 1024 > copy_bytes / 4]
+        return copy_bytes / (sum(v) / len(v) * 1024)
+
+    ff = copy_factor(args.copy_fetch, "FETCH_SIZE")
+    wf = copy_factor(args.copy_write, "WRITE_SIZE")
+    fetch = per_kernel(args.pmc_fetch, "FETCH_SIZE")
+    write = per_kernel(args.pmc_write, "WRITE_SIZE")
+    rows = {}
+    for name, v in fetch.items():
+        kb = kernel_base(name)
+        if kb not in KERNEL_SOURCES:
+            continue
+        w = [x for n, xs in write.items() if kernel_base(n) == kb for x in xs]
+        fk, wk = sum(v) / len(v), (sum(w) / len(w) if w else 0.0)
+        rows[kb] = (fk, wk, fk * 1024 * ff + wk * 1024 * wf)
+    cfg_name = args.config
+    keep = []
+    if os.path.exists(TRAFFIC_FILE):
+        keep = [l for l in open(TRAFFIC_FILE) if not (l.split() and l.split()[0] == cfg_name)]
+    with open(TRAFFIC_FILE, "w") as out:
+        if not keep:
+            out.write("# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch),\n"
+                      "# each scaled by the bytes a plain 1 GiB device copy moves per counted KiB.\n"
+                      "# workload kernel fetch_kib= write_kib= fetch_factor= write_factor= bytes= src=<kernel sources sha256/16>\n")
+        out.writelines(keep)
+        for kb, (fk, wk, b) in sorted(rows.items()):
+            out.write(f"{cfg_name} {kb} fetch_kib={fk:.1f} write_kib={wk:.1f} fetch_factor={ff:.4f} "
+                      f"write_factor={wf:.4f} bytes={b:.0f} src={source_hash(kb)}\n")
+    print(f"wrote {len(rows)} kernel(s) for {cfg_name} to {TRAFFIC_FILE}")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -65,6 +251,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.traffic_from:
+        args.pmc_fetch, args.pmc_write, args.copy_fetch, args.copy_write = args.traffic_from
+        traffic_from(args)
         return
 
     import numpy as np
@@ -156,35 +346,17 @@ def main():
     stages = prof.collect()
     prof.close()
 
-    # algorithmic bytes per launch of each stage
-    mq8 = qr.matrix_bytes(qr.FMT_Q8, F, H)
-    mr_gu, mr_dn = qr.matrix_bytes(fmt, F, H), qr.matrix_bytes(fmt, H, F)
-    sh = 1 if cfg.shared else 0
-    P = T * k + sh * T
-    u_avg = float(np.mean([used[args.warmup + i % G] for i in range(K)]))
-    act_x = T * H + T * (H // 32) * 4
-    act_h = P * F + P * (F // 32) * 4
-    stage_bytes = {
-        "route": (E * H * 4 if cfg.route == "learned" else T * k * 4) + T * H * 4 + act_x,
-        "gateup": u_avg * 2 * mr_gu + sh * 2 * mq8 + act_x + act_h,
-        "down": u_avg * mr_dn + sh * qr.matrix_bytes(qr.FMT_Q8, H, F) + act_h + T * H * 4,
-    }
-    layer_bytes = (u_avg * (2 * mr_gu + mr_dn) + sh * (2 * mq8 + qr.matrix_bytes(qr.FMT_Q8, H, F))
-                   + (E * H * 4 if cfg.route == "learned" else 0) + 2 * T * H * 4)
+    model = stage_model(cfg, qr, u_avg_of(used, args.warmup, G, K))
     dom = max(stages, key=lambda s: stages[s][0])
     dom_us = stages[dom][0] / stages[dom][1] * 1e3
-    dom_bytes = stage_bytes.get(dom)
-    roofline = {
-        "kernel": dom,
-        "bound": "hbm",
-        "achieved": round(dom_bytes / (dom_us * 1e-6) / 1e9, 1) if dom_bytes else None,
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(dom_bytes / (dom_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if dom_bytes else None,
-        "traffic": None,
-        "avg_launch_us": round(dom_us, 3),
-        "algorithmic_bytes_per_launch": int(dom_bytes) if dom_bytes else None,
-    }
+    roofline = make_roofline(cfg, model, dom, dom_us)
+    layer_bytes = model["layer_bytes"]
+    stage_detail = {}
+    for s_, (ms_tot, n_) in stages.items():
+        us = ms_tot / n_ * 1e3
+        b = model["stages"].get(s_, {}).get("bytes")
+        stage_detail[s_] = {"us": round(us, 3), "bytes": int(b) if b else None,
+                            "gbps": round(b / (us * 1e-6) / 1e9, 1) if b else None}
 
     res = {
         "metric": METRIC,
@@ -211,7 +383,7 @@ def main():
         "layer_gbps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
         "layer_hbm_frac": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "eager_ms_per_step": round(eager_ms, 5),
-        "stages_us": {s: round(v[0] / v[1] * 1e3, 3) for s, v in stages.items()},
+        "stages": stage_detail,
         "roofline": roofline,
         "cpu_baseline": None,
         "setup_s": round(time.time() - t_setup, 1),

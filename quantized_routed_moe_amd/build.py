@@ -18,7 +18,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # multiply-adds only where the source asks for one), so every kernel that
 # shares a computation produces the same bits.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-I", os.path.join(ROOT, "include"),
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result",
+         # MFMA results in ordinary VGPRs: the epilogues read every result, and
+         # from AGPRs each read would be one more VALU instruction.
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _compile(src: str) -> str:

@@ -99,22 +99,36 @@ struct moe_prof {
 
 static thread_local moe_prof *t_prof = nullptr;
 
+namespace qrmoe {
+LaunchEvents &launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace qrmoe
+
 namespace {
 
-// Launch helper: brackets the launch with events when a profiler is attached.
+// Launch helper: with a profiler attached, arms an event pair that the
+// stage's kernel launch records its start and end into.
 template <class F>
 hipError_t timed(int stage, hipStream_t s, F &&launch) {
     moe_prof *p = t_prof;
     EventPair ev{nullptr, nullptr, stage};
+    LaunchEvents &armed = launch_events();
     if (p && p->next + 2 <= p->pool.size()) {
         ev.a = p->pool[p->next++];
         ev.b = p->pool[p->next++];
-        hipEventRecord(ev.a, s);
+        armed.start = ev.a;
+        armed.stop = ev.b;
     }
     hipError_t err = launch();
     if (ev.a) {
-        hipEventRecord(ev.b, s);
-        p->used.push_back(ev);
+        if (armed.start == nullptr) {
+            p->used.push_back(ev);  // the stage's kernel took the events
+        } else {
+            armed.start = armed.stop = nullptr;  // no kernel launched: return the pair
+            p->next -= 2;
+        }
     }
     return err;
 }

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_fp16.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -201,6 +202,26 @@ __device__ inline void block_excl_scan(const int *in, int *out, int n, int *tmp_
 }
 
 // ------------------------------------------------------------- launchers
+// Event pair armed by the stage profiler for the next layer kernel launch on
+// this thread.  A launch that finds it armed goes through
+// hipExtLaunchKernelGGL, whose events take the kernel's own start and end
+// times (no dispatch latency), and disarms it.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents &launch_events();
+
+template <class... KArgs, class... Args>
+void klaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
+    LaunchEvents &ev = launch_events();
+    if (ev.start) {
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+        ev.start = ev.stop = nullptr;
+    } else {
+        kernel<<<grid, block, 0, s>>>(args...);
+    }
+}
+
 hipError_t launch_pack(int fmt, const uint8_t *canon, uint8_t *packed, int64_t n_mats, int64_t rows, int64_t cols,
                        hipStream_t s);
 hipError_t launch_check_table(const int32_t *table, int32_t vocab, int32_t k, int32_t E, int32_t *result,

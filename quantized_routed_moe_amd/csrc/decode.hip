@@ -258,7 +258,7 @@ static hipError_t front_h(const LayerArgs &a, hipStream_t s) {
     }
     if (n_lead > 4096) n_lead = 4096;
     const int ns = d.has_shared ? (d.F / GuRows<H, kFmtQ8>::v) * ((d.T + kVecTok - 1) / kVecTok) : 0;
-    decode_front_kernel<H, DUMP><<<dim3(n_lead + ns), dim3(256), 0, s>>>(a, n_lead);
+    klaunch(decode_front_kernel<H, DUMP>, dim3(n_lead + ns), dim3(256), s, a, n_lead);
     return hipGetLastError();
 }
 
@@ -275,14 +275,14 @@ hipError_t launch_decode_front(const LayerArgs &a, bool dump, hipStream_t s) {
 }
 
 hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s) {
-    decode_select_kernel<<<dim3(1), dim3(256), 0, s>>>(a);
+    klaunch(decode_select_kernel, dim3(1), dim3(256), s, a);
     return hipGetLastError();
 }
 
 template <int F, int FMT, bool DUMP>
 static hipError_t down1_h(const LayerArgs &a, hipStream_t s) {
     constexpr int RPW = 64 / DefLpr<F, FMT>::v;
-    decode_down1_kernel<F, FMT, DUMP><<<dim3(a.d.H / (4 * RPW)), dim3(256), 0, s>>>(a);
+    klaunch(decode_down1_kernel<F, FMT, DUMP>, dim3(a.d.H / (4 * RPW)), dim3(256), s, a);
     return hipGetLastError();
 }
 

@@ -84,111 +84,101 @@ __device__ __forceinline__ void score_key(float l, const float *bias, int e, flo
     *key = sc + (bias ? bias[e] : 0.0f);
 }
 
-// Selection order as one integer: larger key first, equal keys smaller
-// expert id first.  The fp32 key's bits are mapped to an order-preserving
-// unsigned integer (IEEE total order on finite values), the id is stored
-// complemented in the low word.
-__device__ __forceinline__ uint64_t sel_code(float key, int e) {
-    uint32_t u = __float_as_uint(key == 0.0f ? 0.0f : key);  // -0 ties with +0
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+// Order-preserving image of an fp32 key in the unsigned integers (IEEE total
+// order on finite values; -0 maps with +0).  Every finite key maps above 0.
+__device__ __forceinline__ uint32_t key_order(float key) {
+    const uint32_t u = __float_as_uint(key == 0.0f ? 0.0f : key);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ void cas_desc(uint64_t &a, uint64_t &b) {
-    const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-    a = hi;
-    b = lo;
-}
-
-// Sort 8 codes descending (bitonic network).
-__device__ __forceinline__ void sort8_desc(uint64_t v[8]) {
-#pragma unroll
-    for (int k = 2; k <= 8; k <<= 1)
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int l = i ^ j;
-                if (l > i) {
-                    if ((i & k) == 0) cas_desc(v[i], v[l]);
-                    else cas_desc(v[l], v[i]);
-                }
-            }
-}
-
-// One wave selects the top-k (k <= 8) experts of one token from its keys
+// One wave selects the top-k (k <= 8 <= E) experts of one token from its keys
 // (larger key first, equal keys: smaller expert id) and weights them by
-// score / sum of the selected scores (summed in rank order).  Each lane sorts
-// its own candidates, then an xor butterfly merges the lanes' top-8 lists:
-// at each level a lane keeps the top 8 of its list and its partner's.
-__device__ void select_keys_wave(const float *__restrict__ krow, const float *__restrict__ srow, int E, int k,
-                                 int32_t *ids_out, float *w_out, int lane) {
-    constexpr int MAXPER = 16;  // E <= 1024
-    const int per = (E + 63) / 64;
-    uint64_t top[8];
-    float my_s[MAXPER];
+// score / sum of the selected scores, summed in rank order.
+//  1. tau = the k-th largest key image, found bit by bit from the top: a bit
+//     is kept when at least k keys are >= the threshold with it set (ballot
+//     counts, uniform scalar work).
+//  2. selected = keys above tau, then keys equal to tau in ascending expert id
+//     until k are taken.
+//  3. each selected expert's rank = number of keys ordered before it; lane
+//     `rank` keeps its id and score, lanes 0..k-1 write the result.
+//  PER candidate slots per lane (64 * PER >= E); slots past E sort below
+//  every key and are never counted or selected.
+template <int PER>
+__device__ void select_keys_per(const float *__restrict__ krow, const float *__restrict__ srow, int E, int k,
+                                int32_t *ids_out, float *w_out, int lane) {
+    uint32_t u[PER];
+    float s[PER];
 #pragma unroll
-    for (int i = 0; i < MAXPER; ++i) {
+    for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        my_s[i] = (i < per && e < E) ? srow[e] : 0.0f;
+        const bool ok = e < E;
+        u[i] = ok ? key_order(krow[e]) : 0u;  // absent candidates sort below every key
+        s[i] = ok ? srow[e] : 0.0f;
+    }
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = tau | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            n += __popcll(__ballot(u[i] >= c));
+        if (n >= k) tau = c;
+    }
+    uint64_t selb[PER];
+    int need = k;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        selb[i] = __ballot(u[i] > tau);
+        need -= __popcll(selb[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) top[i] = 0;  // below every real code
-    // fold this lane's candidates into a sorted top-8 list, 8 at a time
-#pragma unroll
-    for (int base = 0; base < MAXPER; base += 8) {
-        if (base >= per) break;
-        uint64_t c[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = lane + 64 * (base + i);
-            c[i] = (base + i < per && e < E) ? sel_code(krow[e], e) : 0;
+    for (int i = 0; i < PER; ++i) {
+        uint64_t eq = __ballot(u[i] == tau);
+        while (eq && need > 0) {  // lowest lane = smallest id within the slot
+            const uint64_t low = eq & (~eq + 1ull);
+            selb[i] |= low;
+            eq ^= low;
+            --need;
         }
-        sort8_desc(c);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {  // top 8 of two sorted lists form a bitonic sequence
-            const uint64_t m = c[7 - i] > top[i] ? c[7 - i] : top[i];
-            top[i] = m;
-        }
-        sort8_desc(top);
     }
+    int my_id = 0;
+    float my_s = 0.0f;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint64_t other[8];
+    for (int i = 0; i < PER; ++i) {
+        uint64_t m = selb[i];
+        while (m) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t ux = __builtin_amdgcn_readlane(u[i], l);
+            const float sx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[i]), l));
+            const int ex = l + 64 * i;
+            int rank = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t lo = __shfl_xor((uint32_t)top[i], o), hi = __shfl_xor((uint32_t)(top[i] >> 32), o);
-            other[i] = ((uint64_t)hi << 32) | lo;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) top[i] = other[7 - i] > top[i] ? other[7 - i] : top[i];
-        sort8_desc(top);
-    }
-    // every lane holds the same list; fetch each selected score from its owner lane
-    int sel[8];
-    float sc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        sel[j] = (int)(0xFFFFFFFFu - (uint32_t)top[j]);
-        float mine = 0.0f;
-        const int slot = (sel[j] >> 6) & (MAXPER - 1);
-#pragma unroll
-        for (int i = 0; i < MAXPER; ++i)
-            if (i == slot) mine = my_s[i];
-        sc[j] = __shfl(mine, sel[j] & 63);
-    }
-    if (lane == 0) {
-        float S = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < k) S += sc[j];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < k) {
-                ids_out[j] = sel[j];
-                w_out[j] = sc[j] / S;
+            for (int j = 0; j < PER; ++j)
+                rank += __popcll(__ballot(u[j] > ux || (u[j] == ux && lane + 64 * j < ex)));
+            if (lane == rank) {
+                my_id = ex;
+                my_s = sx;
             }
+        }
     }
+    float S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k) S += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
+    if (lane < k) {
+        ids_out[lane] = my_id;
+        w_out[lane] = my_s / S;
+    }
+}
+
+__device__ __forceinline__ void select_keys_wave(const float *__restrict__ krow, const float *__restrict__ srow, int E,
+                                                 int k, int32_t *ids_out, float *w_out, int lane) {
+    if (E <= 64) select_keys_per<1>(krow, srow, E, k, ids_out, w_out, lane);
+    else if (E <= 128) select_keys_per<2>(krow, srow, E, k, ids_out, w_out, lane);
+    else if (E <= 256) select_keys_per<4>(krow, srow, E, k, ids_out, w_out, lane);
+    else if (E <= 512) select_keys_per<8>(krow, srow, E, k, ids_out, w_out, lane);
+    else select_keys_per<16>(krow, srow, E, k, ids_out, w_out, lane);
 }
 
 __device__ void select_hash_wave(const int32_t *__restrict__ token_ids, const int32_t *__restrict__ table, int t,

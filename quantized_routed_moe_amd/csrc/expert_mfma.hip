@@ -283,11 +283,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(LayerArgs a) {
 template <bool DUMP>
 static hipError_t gateup_m(const LayerArgs &a, dim3 grid, hipStream_t s) {
     switch (a.d.H) {
-        case 256: gateup_mfma_kernel<256, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 512: gateup_mfma_kernel<512, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 1024: gateup_mfma_kernel<1024, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 2048: gateup_mfma_kernel<2048, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 4096: gateup_mfma_kernel<4096, DUMP><<<grid, 256, 0, s>>>(a); break;
+        case 256: klaunch(gateup_mfma_kernel<256, DUMP>, grid, 256, s, a); break;
+        case 512: klaunch(gateup_mfma_kernel<512, DUMP>, grid, 256, s, a); break;
+        case 1024: klaunch(gateup_mfma_kernel<1024, DUMP>, grid, 256, s, a); break;
+        case 2048: klaunch(gateup_mfma_kernel<2048, DUMP>, grid, 256, s, a); break;
+        case 4096: klaunch(gateup_mfma_kernel<4096, DUMP>, grid, 256, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -302,11 +302,11 @@ hipError_t launch_gateup_mfma(const LayerArgs &a, int max_tiles, bool dump, hipS
 template <bool DUMP>
 static hipError_t down_m(const LayerArgs &a, dim3 grid, hipStream_t s) {
     switch (a.d.F) {
-        case 256: down_mfma_kernel<256, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 512: down_mfma_kernel<512, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 1024: down_mfma_kernel<1024, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 2048: down_mfma_kernel<2048, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 4096: down_mfma_kernel<4096, DUMP><<<grid, 256, 0, s>>>(a); break;
+        case 256: klaunch(down_mfma_kernel<256, DUMP>, grid, 256, s, a); break;
+        case 512: klaunch(down_mfma_kernel<512, DUMP>, grid, 256, s, a); break;
+        case 1024: klaunch(down_mfma_kernel<1024, DUMP>, grid, 256, s, a); break;
+        case 2048: klaunch(down_mfma_kernel<2048, DUMP>, grid, 256, s, a); break;
+        case 4096: klaunch(down_mfma_kernel<4096, DUMP>, grid, 256, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -114,47 +114,51 @@ __global__ __launch_bounds__(256) void down_vec_kernel(LayerArgs a) {
 }
 
 // out[t][r] = sum over t's experts in ascending id of y[t*k + j][r], then the
-// shared expert's y.  Workgroup (x, y) covers 32 rows x 8 tokens.
-__device__ __forceinline__ void combine_rows(const LayerArgs &a, int r0, int nrows, int t0, int t1) {
-    const Dims &d = a.d;
-    for (int idx = threadIdx.x; idx < (t1 - t0) * nrows; idx += 256) {
-        const int t = t0 + idx / nrows, r = r0 + idx % nrows;
-        const int32_t *ids = a.ws.ids + t * d.k;
-        float acc = 0.0f;
-        int prev = -1;
-        for (int step = 0; step < d.k; ++step) {
-            int best = 0x7fffffff, bj = 0;
-            for (int j = 0; j < d.k; ++j) {
-                const int e = ids[j];
-                if (e > prev && e < best) {
-                    best = e;
-                    bj = j;
-                }
-            }
-            if (best == 0x7fffffff) break;  // a repeated id (unchecked hash table) is summed once
-            acc = __fadd_rn(acc, a.ws.y[(int64_t)(t * d.k + bj) * d.H + r]);
-            prev = best;
-        }
-        if (d.has_shared) acc = __fadd_rn(acc, a.ws.y[(int64_t)(d.T * d.k + t) * d.H + r]);
-        a.out[(int64_t)t * d.H + r] = acc;
-    }
-}
-
+// shared expert's y.  Workgroup (x, t): rows [1024x, 1024x + 1024) of token t,
+// 4 consecutive rows per thread; the token's order of experts is found once.
 __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
-    const int t0 = blockIdx.y * 8;
-    combine_rows(a, blockIdx.x * kVecRows, kVecRows, t0, min(t0 + 8, a.d.T));
+    const Dims &d = a.d;
+    const int t = blockIdx.y;
+    const int r = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (r >= d.H) return;
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = j < d.k ? a.ws.ids[t * d.k + j] : 0x7fffffff;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto add = [&](int64_t pair) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.ws.y + pair * d.H + r);
+        acc.x = __fadd_rn(acc.x, v.x);
+        acc.y = __fadd_rn(acc.y, v.y);
+        acc.z = __fadd_rn(acc.z, v.z);
+        acc.w = __fadd_rn(acc.w, v.w);
+    };
+    int prev = -1;
+    for (int step = 0; step < d.k; ++step) {
+        int best = 0x7fffffff, bj = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (e[j] > prev && e[j] < best) {
+                best = e[j];
+                bj = j;
+            }
+        if (best == 0x7fffffff) break;  // a repeated id (unchecked hash table) is summed once
+        add((int64_t)t * d.k + bj);
+        prev = best;
+    }
+    if (d.has_shared) add((int64_t)d.T * d.k + t);
+    *reinterpret_cast<float4 *>(a.out + (int64_t)t * d.H + r) = acc;
 }
 
 // ------------------------------------------------------------- launchers
 template <int FMT, bool DUMP, bool SKIP>
 static hipError_t gateup_k(const LayerArgs &a, dim3 grid, hipStream_t s) {
     switch (a.d.H) {
-        case 128: if constexpr (FMT == kFmtQ8) { gateup_vec_kernel<128, FMT, DUMP, SKIP><<<grid, 256, 0, s>>>(a); break; } return hipErrorInvalidValue;
-        case 256: if constexpr (FMT == kFmtQ8) { gateup_vec_kernel<256, FMT, DUMP, SKIP><<<grid, 256, 0, s>>>(a); break; } return hipErrorInvalidValue;
-        case 512: gateup_vec_kernel<512, FMT, DUMP, SKIP><<<grid, 256, 0, s>>>(a); break;
-        case 1024: gateup_vec_kernel<1024, FMT, DUMP, SKIP><<<grid, 256, 0, s>>>(a); break;
-        case 2048: gateup_vec_kernel<2048, FMT, DUMP, SKIP><<<grid, 256, 0, s>>>(a); break;
-        case 4096: gateup_vec_kernel<4096, FMT, DUMP, SKIP><<<grid, 256, 0, s>>>(a); break;
+        case 128: if constexpr (FMT == kFmtQ8) { klaunch(gateup_vec_kernel<128, FMT, DUMP, SKIP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
+        case 256: if constexpr (FMT == kFmtQ8) { klaunch(gateup_vec_kernel<256, FMT, DUMP, SKIP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
+        case 512: klaunch(gateup_vec_kernel<512, FMT, DUMP, SKIP>, grid, 256, s, a); break;
+        case 1024: klaunch(gateup_vec_kernel<1024, FMT, DUMP, SKIP>, grid, 256, s, a); break;
+        case 2048: klaunch(gateup_vec_kernel<2048, FMT, DUMP, SKIP>, grid, 256, s, a); break;
+        case 4096: klaunch(gateup_vec_kernel<4096, FMT, DUMP, SKIP>, grid, 256, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -175,12 +179,12 @@ hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool skip_share
 template <int FMT, bool DUMP>
 static hipError_t down_k(const LayerArgs &a, dim3 grid, hipStream_t s) {
     switch (a.d.F) {
-        case 128: if constexpr (FMT == kFmtQ8) { down_vec_kernel<128, FMT, DUMP><<<grid, 256, 0, s>>>(a); break; } return hipErrorInvalidValue;
-        case 256: if constexpr (FMT == kFmtQ8) { down_vec_kernel<256, FMT, DUMP><<<grid, 256, 0, s>>>(a); break; } return hipErrorInvalidValue;
-        case 512: down_vec_kernel<512, FMT, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 1024: down_vec_kernel<1024, FMT, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 2048: down_vec_kernel<2048, FMT, DUMP><<<grid, 256, 0, s>>>(a); break;
-        case 4096: down_vec_kernel<4096, FMT, DUMP><<<grid, 256, 0, s>>>(a); break;
+        case 128: if constexpr (FMT == kFmtQ8) { klaunch(down_vec_kernel<128, FMT, DUMP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
+        case 256: if constexpr (FMT == kFmtQ8) { klaunch(down_vec_kernel<256, FMT, DUMP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
+        case 512: klaunch(down_vec_kernel<512, FMT, DUMP>, grid, 256, s, a); break;
+        case 1024: klaunch(down_vec_kernel<1024, FMT, DUMP>, grid, 256, s, a); break;
+        case 2048: klaunch(down_vec_kernel<2048, FMT, DUMP>, grid, 256, s, a); break;
+        case 4096: klaunch(down_vec_kernel<4096, FMT, DUMP>, grid, 256, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -193,7 +197,7 @@ hipError_t launch_down_vec(const LayerArgs &a, int max_groups, bool dump, hipStr
 }
 
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s) {
-    combine_kernel<<<dim3(a.d.H / kVecRows, (a.d.T + 7) / 8), dim3(256), 0, s>>>(a);
+    klaunch(combine_kernel, dim3((a.d.H + 1023) / 1024, a.d.T), dim3(256), s, a);
     return hipGetLastError();
 }
 

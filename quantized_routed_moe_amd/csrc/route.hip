@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void quant_kernel(LayerArgs a) {
 hipError_t launch_quant(const LayerArgs &a, hipStream_t s) {
     int blocks = (a.d.T * (a.d.H / 32) + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    quant_kernel<<<dim3(blocks), dim3(256), 0, s>>>(a);
+    klaunch(quant_kernel, dim3(blocks), dim3(256), s, a);
     return hipGetLastError();
 }
 
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(LayerArgs a) {
 hipError_t launch_logits(const LayerArgs &a, hipStream_t s) {
     if (a.d.H < kLogChunk || a.d.H > kLogChunk * 64) return hipErrorInvalidValue;
     dim3 grid((a.d.T + kLogTile - 1) / kLogTile, (a.d.E + kLogTile - 1) / kLogTile);
-    logits_tiled_kernel<<<grid, dim3(256), 0, s>>>(a);
+    klaunch(logits_tiled_kernel, grid, dim3(256), s, a);
     return hipGetLastError();
 }
 
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void select_kernel(LayerArgs a) {
 
 
 hipError_t launch_select(const LayerArgs &a, hipStream_t s) {
-    select_kernel<<<dim3((a.d.T + 3) / 4), dim3(256), 0, s>>>(a);
+    klaunch(select_kernel, dim3((a.d.T + 3) / 4), dim3(256), s, a);
     return hipGetLastError();
 }
 
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void sort_kernel(LayerArgs a) {
 }
 
 hipError_t launch_sort(const LayerArgs &a, hipStream_t s) {
-    sort_kernel<<<dim3(1), dim3(256), 0, s>>>(a);
+    klaunch(sort_kernel, dim3(1), dim3(256), s, a);
     return hipGetLastError();
 }
 

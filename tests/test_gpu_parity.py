@@ -180,7 +180,7 @@ def test_skewed_bias_sends_all_tokens_to_one_expert():
 
 
 def test_skewed_bias_mfma_tiles():
-    """One expert takes every token: 200 pairs cut into seven 32-pair MFMA tiles (last one ragged)."""
+    """One expert takes every token: 200 pairs cut into four 64-pair MFMA tiles (last one ragged)."""
     cfg = ms.LayerConfig("skew_mfma", 512, 16, 2, 256, 200, seed=29)
     inp = ms.make_inputs(cfg)
     inp["router_b"][3] = 10.0
@@ -188,6 +188,24 @@ def test_skewed_bias_mfma_tiles():
     g = run_gpu(cfg, inp, layer, stride=4)
     assert g["counts"][3] == 200
     check(cfg, inp, g, stride=4, name="skew_mfma")
+
+
+@pytest.mark.parametrize("T", [1, 7, 40])
+def test_tied_keys_take_the_smaller_expert_ids(T):
+    """Experts share router rows and biases in groups of four, so every
+    token's top-6 boundary falls inside a group of equal keys: the two
+    smaller ids of that group are taken (decode select for T <= 32, the
+    batched select above)."""
+    cfg = ms.LayerConfig(f"ties_T{T}", 512, 64, 6, 256, T, seed=33)
+    inp = ms.make_inputs(cfg)
+    inp["router_w"] = np.ascontiguousarray(np.repeat(inp["router_w"][::4], 4, axis=0))
+    inp["router_b"] = np.ascontiguousarray(np.repeat(inp["router_b"][::4], 4))
+    layer = _qr().MoELayer(512, 64, 6, 256).load(inp)
+    g = run_gpu(cfg, inp, layer, stride=4)
+    groups = g["ids"].reshape(T, 6) // 4
+    for row in groups:  # one whole group of four plus two of the next
+        assert sorted(np.bincount(row).tolist())[-2:] == [2, 4], row
+    check(cfg, inp, g, stride=4, name=f"ties_T{T}")
 
 
 def test_max_tokens_small_shape():
