@@ -179,8 +179,9 @@ int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 int moe_workspace_flags(void *workspace, int32_t *flags, void *stream);
 
 /* Per-stage timing with HIP events.  While a profiler is attached to the
- * calling thread, every kernel a forward call launches is bracketed by two
- * events on the call's stream.  moe_prof_collect waits for the recorded
+ * calling thread, every kernel a forward call launches records its own start
+ * and end into two events (hipExtLaunchKernelGGL; dispatch latency between
+ * kernels is not counted).  moe_prof_collect waits for the recorded
  * events, adds the elapsed milliseconds and launch counts per stage into the
  * caller's arrays (n_stages entries, index = stage id) and forgets them. */
 typedef struct moe_prof moe_prof;
