@@ -54,6 +54,7 @@ Layout make_layout(const moe_shape *s, int64_t T) {
     int64_t G = max_groups(s, T, kVecTok);
     const int64_t G2 = max_groups(s, T, kMfmaTile);
     if (G2 > G) G = G2;
+    if (G < 16) G = 16;  // the one-token down kernel reads the first 8 entries unconditionally
     Layout L{};
     size_t o = 0;
     auto take = [&](size_t bytes) {

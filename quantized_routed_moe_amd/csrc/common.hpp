@@ -9,6 +9,8 @@
 
 namespace qrmoe {
 
+typedef __attribute__((address_space(3))) void *lds_ptr;  // LDS address for global->LDS loads
+
 constexpr int kWave = 64;
 constexpr int kThreads = 256;       // every kernel runs 4 waves per workgroup
 constexpr int kVecTok = 8;          // tokens per work group of the VALU expert kernels
@@ -58,7 +60,7 @@ struct Ws {
     int32_t *counts;
     int32_t *offsets;
     int32_t *perm;
-    int4 *groups;    // {expert (E = shared), first index into perm (or first token), count, 0}
+    int4 *groups;    // {expert (E = shared), first index into perm (or first token), count, first pair}
     int8_t *hq;
     float *hd;
     float *y;        // [P][H] weighted expert outputs (w already applied)
@@ -128,46 +130,61 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
     return (int)r;
 }
 
+// One 32-block of fp32 values held in registers (loaded apart from the
+// quantization so a kernel can request it before a long weight stream).
+struct QBlock {
+    float v[32];
+    __device__ __forceinline__ void load(const float *__restrict__ x, int64_t blk) {
+        const float4 *src = reinterpret_cast<const float4 *>(x + blk * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 f = src[i];
+            v[4 * i] = f.x;
+            v[4 * i + 1] = f.y;
+            v[4 * i + 2] = f.z;
+            v[4 * i + 3] = f.w;
+        }
+    }
+    // codes -> xq[blk*32 ..], scale -> xd[blk], (xs16) code sums of the two 16-halves
+    __device__ __forceinline__ void store(int8_t *__restrict__ xq, float *__restrict__ xd, int32_t *__restrict__ xs16,
+                                         int64_t blk) const {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const float d = quant_scale(amax);
+        const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+        uint32_t words[8];
+        int s0 = 0, s1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t wv = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int q = quant_code(v[4 * i + c], inv);
+                if (i < 4) s0 += q;
+                else s1 += q;
+                wv |= ((uint32_t)q & 0xffu) << (8 * c);
+            }
+            words[i] = wv;
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(xq + blk * 32);
+        dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+        dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+        xd[blk] = d;
+        if (xs16) {
+            xs16[2 * blk] = s0;
+            xs16[2 * blk + 1] = s1;
+        }
+    }
+};
+
 // One thread quantizes the 32-block `blk` of x into codes, scale and (when
 // xs16 is given) the two 16-subblock code sums.
 __device__ __forceinline__ void quant_one_block(const float *__restrict__ x, int8_t *__restrict__ xq,
                                                 float *__restrict__ xd, int32_t *__restrict__ xs16, int64_t blk) {
-    const float4 *src = reinterpret_cast<const float4 *>(x + blk * 32);
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float4 f = src[i];
-        v[4 * i] = f.x;
-        v[4 * i + 1] = f.y;
-        v[4 * i + 2] = f.z;
-        v[4 * i + 3] = f.w;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const float d = quant_scale(amax);
-    const float inv = d > 0.0f ? 1.0f / d : 0.0f;
-    uint32_t words[8];
-    int s0 = 0, s1 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t wv = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            int q = quant_code(v[4 * i + c], inv);
-            if (i < 4) s0 += q; else s1 += q;
-            wv |= ((uint32_t)q & 0xffu) << (8 * c);
-        }
-        words[i] = wv;
-    }
-    uint4 *dst = reinterpret_cast<uint4 *>(xq + blk * 32);
-    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
-    xd[blk] = d;
-    if (xs16) {
-        xs16[2 * blk] = s0;
-        xs16[2 * blk + 1] = s1;
-    }
+    QBlock q;
+    q.load(x, blk);
+    q.store(xq, xd, xs16, blk);
 }
 
 // Exclusive scan of n <= 1024 ints in LDS (in place into `out`), 256 threads.

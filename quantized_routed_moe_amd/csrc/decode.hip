@@ -75,13 +75,19 @@ __global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_le
     const int s = blockIdx.x - n_lead, nrc = d.F / ROWS;
     const int rc = s % nrc, t0 = (s / nrc) * kVecTok;
     const int cnt = min(kVecTok, d.T - t0);
-    for (int b = tid; b < cnt * (H / 32); b += 256) {
-        const int tok = b / (H / 32), blk = b % (H / 32);
-        quant_one_block(a.x + (int64_t)(t0 + tok) * H, sm.vs.aq[tok], sm.vs.ad[tok], nullptr, blk);
-    }
-    if (tid < cnt) sm.vs.pair[tid] = d.T * d.k + t0 + tid;
-    __syncthreads();
-    gateup_rows<H, kFmtQ8, kVecTok, ROWS, false, DUMP>(a, sm.vs, a.wt.sh_gate, a.wt.sh_up, cnt, rc * ROWS);
+    // each thread's first x block is requested before the weight rows
+    QBlock xb;
+    const bool first = tid < cnt * (H / 32);
+    if (first) xb.load(a.x + (int64_t)(t0 + tid / (H / 32)) * H, tid % (H / 32));
+    gateup_rows<H, kFmtQ8, kVecTok, ROWS, false, DUMP>(a, sm.vs, a.wt.sh_gate, a.wt.sh_up, cnt, rc * ROWS, [&] {
+        if (first) xb.store(sm.vs.aq[tid / (H / 32)], sm.vs.ad[tid / (H / 32)], nullptr, tid % (H / 32));
+        for (int b = tid + 256; b < cnt * (H / 32); b += 256) {
+            const int tok = b / (H / 32), blk = b % (H / 32);
+            quant_one_block(a.x + (int64_t)(t0 + tok) * H, sm.vs.aq[tok], sm.vs.ad[tok], nullptr, blk);
+        }
+        if (tid < cnt) sm.vs.pair[tid] = d.T * d.k + t0 + tid;
+        __syncthreads();
+    });
 }
 
 // ----------------------------------------------------------------- select
@@ -163,11 +169,11 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
     const int G = rs.ngroups;
     for (int g = tid; g < G; g += 256) {
         const int gs = rs.gpos[g], ge = g + 1 < G ? rs.gpos[g + 1] : P;
-        a.ws.groups[g] = make_int4(rs.ids[rs.perm[gs]], gs, ge - gs, 0);
+        a.ws.groups[g] = make_int4(rs.ids[rs.perm[gs]], gs, ge - gs, rs.perm[gs]);
     }
     const int ns = d.has_shared ? (d.T + kVecTok - 1) / kVecTok : 0;
     for (int j = tid; j < ns; j += 256)
-        a.ws.groups[G + j] = make_int4(d.E, j * kVecTok, min(kVecTok, d.T - j * kVecTok), 0);
+        a.ws.groups[G + j] = make_int4(d.E, j * kVecTok, min(kVecTok, d.T - j * kVecTok), P + j * kVecTok);
     if (tid == 0) {
         a.ws.ctl[kCtlGroups] = G + ns;
         a.ws.offsets[d.E] = P;
@@ -193,29 +199,87 @@ template <int F, int FMT, bool DUMP>
 __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
     constexpr int L = DefLpr<F, FMT>::v;
     constexpr int RPW = 64 / L;
+    constexpr int NS = (kMaxSel * (F / 32) + 255) / 256;  // h block scales per thread
     __shared__ VecSmem<F, kMaxSel> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
-    const int G = a.ws.ctl[kCtlGroups];  // k routed groups (ascending id), then the shared expert
-    const int nr = d.has_shared ? G - 1 : G;
     const int seg = lane % L, r = (blockIdx.x * 4 + wave) * RPW + lane / L;
+    // Loads are issued in the order their results are needed, because a wave
+    // waits for loads in issue order: the shared expert's row (needs no
+    // routing), the work list, the h rows and combine weights of the groups,
+    // then the routed rows; h is written to LDS while the rows still stream.
+    RowRegs<F, kFmtQ8, L> rsh;
+    if (d.has_shared) rsh.load(a.wt.sh_down, d.H, r, seg);
+    // k routed groups in ascending id, then the shared expert (the list holds at least kMaxSel entries)
+    const int4 *__restrict__ glist = a.ws.groups;
+    int gx[kMaxSel], gp[kMaxSel];
+#pragma unroll
+    for (int i = 0; i < kMaxSel; ++i) {
+        const int4 g = glist[i];
+        gx[i] = g.x;
+        gp[i] = g.w;  // first (only) pair of the group
+    }
+    const int G = a.ws.ctl[kCtlGroups];
+    const int nr = d.has_shared ? G - 1 : G;
+    // pair of group `i` by a chain of selects (constant register indices)
+    int pown = gp[0];
+#pragma unroll
+    for (int j = 1; j < kMaxSel; ++j) pown = tid == j ? gp[j] : pown;
+    float wown = 1.0f;
+    if (tid < nr) wown = a.ws.w[pown];
+    // h block scales: loads now, LDS after the rows are requested
+    float hdv[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int idx = tid + 256 * u;
+        const bool ok = idx < G * (F / 32);
+        const int tok = ok ? idx / (F / 32) : 0;
+        int p = gp[0];
+#pragma unroll
+        for (int j = 1; j < kMaxSel; ++j) p = tok == j ? gp[j] : p;
+        hdv[u] = a.ws.hd[(int64_t)p * (F / 32) + (ok ? idx % (F / 32) : 0)];
+    }
+    // h codes of the G pairs go straight to LDS (aq rows are contiguous): one
+    // 1 KB global->LDS load per wave instruction, each lane 16 bytes of its own
+    // pair's row; G*F is a multiple of 1 KB for F >= 1024
+    if constexpr (F >= 1024) {
+        const int ninst = G * F / 1024;
+        for (int j = wave; j < ninst; j += 4) {
+            const int o = j * 1024 + lane * 16;
+            const int tok = o / F;
+            int p = gp[0];
+#pragma unroll
+            for (int jj = 1; jj < kMaxSel; ++jj) p = tok == jj ? gp[jj] : p;
+            __builtin_amdgcn_global_load_lds(a.ws.hq + (int64_t)p * F + o % F,
+                                             (lds_ptr)(&sm.aq[0][0] + j * 1024), 16, 0, 0);
+        }
+    }
+    // Every slot loads without a branch (a slot past the routed groups re-reads
+    // group 0's row, served by the cache), so nothing is sunk below the rows.
     const int64_t mb = mat_bytes(FMT, d.H, F);
     RowRegs<F, FMT, L> rr[kMaxSel - 1];
-    RowRegs<F, kFmtQ8, L> rsh;
 #pragma unroll
-    for (int i = 0; i < kMaxSel - 1; ++i)
-        if (i < nr) rr[i].load(a.wt.down + (int64_t)a.ws.groups[i].x * mb, d.H, r, seg);
-    if (d.has_shared) rsh.load(a.wt.sh_down, d.H, r, seg);
+    for (int i = 0; i < kMaxSel - 1; ++i) rr[i].load(a.wt.down + (int64_t)(i < nr ? gx[i] : gx[0]) * mb, d.H, r, seg);
     if (tid < G) {
-        const int4 grp = a.ws.groups[tid];
-        const bool shared = grp.x == d.E;
-        const int p = shared ? d.k : a.ws.perm[grp.y];
-        sm.pair[tid] = p;
-        sm.row[tid] = p;
-        sm.w[tid] = shared ? 1.0f : a.ws.w[p];
+        sm.pair[tid] = pown;
+        sm.w[tid] = wown;
     }
-    __syncthreads();
-    stage_rows<F, kMaxSel, false>(sm, a.ws.hq, a.ws.hd, nullptr, G);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int idx = tid + 256 * u;
+        if (idx < G * (F / 32)) sm.ad[idx / (F / 32)][idx % (F / 32)] = hdv[u];
+    }
+    if constexpr (F < 1024) {
+        for (int i = tid; i < G * (F / 16); i += 256) {
+            const int tok = i / (F / 16);
+            int p = gp[0];
+#pragma unroll
+            for (int jj = 1; jj < kMaxSel; ++jj) p = tok == jj ? gp[jj] : p;
+            reinterpret_cast<int4 *>(sm.aq[tok])[i % (F / 16)] =
+                reinterpret_cast<const int4 *>(a.ws.hq + (int64_t)p * F)[i % (F / 16)];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's global->LDS loads have landed (the rows too)
     __syncthreads();
     if constexpr (FMT == kFmtQ2) {
         subblock_sums(sm, G);

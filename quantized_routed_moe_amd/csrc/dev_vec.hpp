@@ -41,19 +41,28 @@ struct Geo {
 template <int K, int FMT, int LPR>
 struct RowRegs;
 
+// Scales stay as raw fp16 bits until the dot product uses them: converting at
+// load time would make the wave wait for the loads it has just issued (loads
+// retire in order), which turns a prefetch into a synchronous read.
 template <int K, int LPR>
 struct RowRegs<K, kFmtQ8, LPR> {
     static constexpr int J = Geo<K, kFmtQ8, LPR>::J;
     int4 c[J];
-    float s[J];
+    uint32_t s16[J];  // one zero-extended fp16 per register (no packing, which would wait for the load)
     __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, int64_t R, int64_t r, int seg) {
         const int4 *codes = reinterpret_cast<const int4 *>(mat + r * K);
         const uint16_t *sc = reinterpret_cast<const uint16_t *>(mat + R * K) + r * (K / 32);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             c[j] = load_stream16(codes + seg + LPR * j);
-            s[j] = f16_to_f32(sc[(seg + LPR * j) >> 1]);
+            s16[j] = sc[(seg + LPR * j) >> 1];
         }
+    }
+    // the empty asm keeps the conversion (and so the wait for the load) at the use
+    __device__ __forceinline__ float scale(int j) const {
+        uint32_t v = s16[j];
+        asm volatile("" : "+v"(v));
+        return f16_to_f32((uint16_t)v);
     }
 };
 
@@ -61,15 +70,19 @@ template <int K, int LPR>
 struct RowRegs<K, kFmtQ2, LPR> {
     int4 c;
     uint32_t sm;
-    float d, dmin;
+    uint32_t dd;  // fp16 d (low half), fp16 dmin (high half)
     __device__ __forceinline__ void load(const uint8_t *__restrict__ mat, int64_t R, int64_t r, int seg) {
         c = load_stream16(reinterpret_cast<const int4 *>(mat + r * (K / 4)) + seg);
         sm = *reinterpret_cast<const uint32_t *>(mat + R * K / 4 + r * (K / 16) + 4 * seg);
-        const uint32_t dd =
-            *reinterpret_cast<const uint32_t *>(mat + R * K / 4 + R * K / 16 + (r * (K / 256) + seg / 4) * 4);
-        d = f16_to_f32((uint16_t)(dd & 0xffff));
-        dmin = f16_to_f32((uint16_t)(dd >> 16));
+        dd = *reinterpret_cast<const uint32_t *>(mat + R * K / 4 + R * K / 16 + (r * (K / 256) + seg / 4) * 4);
     }
+    __device__ __forceinline__ uint32_t raw() const {
+        uint32_t v = dd;
+        asm volatile("" : "+v"(v));  // keeps the conversion (and the wait for the load) at the use
+        return v;
+    }
+    __device__ __forceinline__ float d() const { return f16_to_f32((uint16_t)(raw() & 0xffff)); }
+    __device__ __forceinline__ float dmin() const { return f16_to_f32((uint16_t)(raw() >> 16)); }
 };
 
 // Partial dot of one lane's part of a row with a quantized activation row
@@ -91,7 +104,7 @@ __device__ __forceinline__ float lane_dot(const RowRegs<K, kFmtQ8, LPR> &w, cons
         I = sdot4(w.c[j].y, x.y, I);
         I = sdot4(w.c[j].z, x.z, I);
         I = sdot4(w.c[j].w, x.w, I);
-        acc = __fmaf_rn((float)I, __fmul_rn(w.s[j], ad[chunk >> 1]), acc);
+        acc = __fmaf_rn((float)I, __fmul_rn(w.scale(j), ad[chunk >> 1]), acc);
         if (dump) {
             const int full = I + __shfl_xor(I, 1);
             if ((seg & 1) == 0) dump[chunk >> 1] = full;
@@ -120,29 +133,30 @@ __device__ __forceinline__ float lane_dot(const RowRegs<K, kFmtQ2, LPR> &w, cons
         if (dump) dump[4 * seg + jj] = P;
     }
     // explicit roundings: the same value in every kernel that inlines this
-    const float b0 = __fsub_rn(__fmul_rn(w.d, (float)SP[0]), __fmul_rn(w.dmin, (float)SM[0]));
-    const float b1 = __fsub_rn(__fmul_rn(w.d, (float)SP[1]), __fmul_rn(w.dmin, (float)SM[1]));
+    const float wd = w.d(), wm = w.dmin();
+    const float b0 = __fsub_rn(__fmul_rn(wd, (float)SP[0]), __fmul_rn(wm, (float)SM[0]));
+    const float b1 = __fsub_rn(__fmul_rn(wd, (float)SP[1]), __fmul_rn(wm, (float)SM[1]));
     return __fadd_rn(__fmul_rn(ad[2 * seg], b0), __fmul_rn(ad[2 * seg + 1], b1));
 }
 
 // Copy the quantized rows `rows[0..cnt)` of (q, dq, s16) into LDS slots 0..cnt.
+// Each iteration requests its code chunk, scale and subblock sum together
+// before storing them, so a wave waits for its loads once per iteration.
 template <int K, int NTOK, bool S16>
 __device__ __forceinline__ void stage_rows(VecSmem<K, NTOK> &sm, const int8_t *__restrict__ q,
                                            const float *__restrict__ dq, const int32_t *__restrict__ s16, int cnt) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < cnt * (K / 16); i += 256) {
+    for (int i = threadIdx.x; i < cnt * (K / 16); i += 256) {
         const int tok = i / (K / 16), c = i % (K / 16);
-        reinterpret_cast<int4 *>(sm.aq[tok])[c] = reinterpret_cast<const int4 *>(q + (int64_t)sm.row[tok] * K)[c];
-    }
-    for (int i = tid; i < cnt * (K / 32); i += 256) {
-        const int tok = i / (K / 32), b = i % (K / 32);
-        sm.ad[tok][b] = dq[(int64_t)sm.row[tok] * (K / 32) + b];
-    }
-    if constexpr (S16) {
-        for (int i = tid; i < cnt * (K / 16); i += 256) {
-            const int tok = i / (K / 16), g = i % (K / 16);
-            sm.as16[tok][g] = s16[(int64_t)sm.row[tok] * (K / 16) + g];
-        }
+        const int4 v = reinterpret_cast<const int4 *>(q + (int64_t)sm.row[tok] * K)[c];
+        const bool has_scale = i < cnt * (K / 32);
+        const int stok = i / (K / 32), b = i % (K / 32);
+        float sc = 0.0f;
+        if (has_scale) sc = dq[(int64_t)sm.row[stok] * (K / 32) + b];
+        int32_t sum16 = 0;
+        if constexpr (S16) sum16 = s16[(int64_t)sm.row[tok] * (K / 16) + c];
+        reinterpret_cast<int4 *>(sm.aq[tok])[c] = v;
+        if (has_scale) sm.ad[stok][b] = sc;
+        if constexpr (S16) sm.as16[tok][c] = sum16;
     }
 }
 
@@ -175,27 +189,38 @@ struct GuRows {
 // (ROWS == 32) into hq/hd; otherwise store h in fp32 for the consumer to
 // quantize (the same values give the same codes wherever they are
 // quantized).  sm.pair[] names the output pair of each token.
-template <int K, int FMT, int NTOK, int ROWS, bool QUANT, bool DUMP>
+//
+// Each wave keeps the rows of the next two passes in flight.  The first two
+// are requested before `stage()` runs (the caller's activation staging, which
+// ends with a barrier), so weight streaming starts as soon as the expert is
+// known.
+template <int K, int FMT, int NTOK, int ROWS, bool QUANT, bool DUMP, class Stage>
 __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint8_t *__restrict__ gmat,
-                            const uint8_t *__restrict__ umat, int cnt, int r0) {
+                            const uint8_t *__restrict__ umat, int cnt, int r0, Stage stage) {
     using G = Geo<K, FMT>;
+    using RR = RowRegs<K, FMT, G::L>;
     constexpr int PASSES = ROWS / (4 * G::RPW);
     static_assert(PASSES >= 1 && ROWS % (4 * G::RPW) == 0 && (!QUANT || ROWS == kVecRows), "row geometry");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int seg = lane % G::L, rsub = lane / G::L;
-    RowRegs<K, FMT, G::L> wg, wu;
-    int row_local = wave * G::RPW + rsub;
-    wg.load(gmat, d.F, r0 + row_local, seg);
-    wu.load(umat, d.F, r0 + row_local, seg);
-#pragma unroll 1
+    auto row_of = [&](int pass) { return (pass * 4 + wave) * G::RPW + rsub; };
+    RR wg0, wu0, wg1, wu1;
+    wg0.load(gmat, d.F, r0 + row_of(0), seg);
+    wu0.load(umat, d.F, r0 + row_of(0), seg);
+    if (PASSES > 1) {
+        wg1.load(gmat, d.F, r0 + row_of(1), seg);
+        wu1.load(umat, d.F, r0 + row_of(1), seg);
+    }
+    stage();
+#pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-        RowRegs<K, FMT, G::L> ng, nu;
-        const int next_local = ((pass + 1) * 4 + wave) * G::RPW + rsub;
-        if (pass + 1 < PASSES) {
-            ng.load(gmat, d.F, r0 + next_local, seg);
-            nu.load(umat, d.F, r0 + next_local, seg);
+        RR ng, nu;
+        if (pass + 2 < PASSES) {
+            ng.load(gmat, d.F, r0 + row_of(pass + 2), seg);
+            nu.load(umat, d.F, r0 + row_of(pass + 2), seg);
         }
+        const int row_local = row_of(pass);
         const int r = r0 + row_local;
         const bool dump_row = DUMP && (r % a.dump.stride == 0);
         for (int tok = 0; tok < cnt; ++tok) {
@@ -206,8 +231,8 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
                 dg = a.dump.gate_sums + base;
                 du = a.dump.up_sums + base;
             }
-            const float gp = group_sum<G::L>(lane_dot<K, G::L>(wg, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dg));
-            const float up = group_sum<G::L>(lane_dot<K, G::L>(wu, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, du));
+            const float gp = group_sum<G::L>(lane_dot<K, G::L>(wg0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dg));
+            const float up = group_sum<G::L>(lane_dot<K, G::L>(wu0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, du));
             if (seg == 0) {
                 const float hv = swiglu(gp, up);
                 if constexpr (QUANT)
@@ -216,11 +241,10 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
                     a.ws.h[(int64_t)sm.pair[tok] * d.F + r] = hv;
             }
         }
-        if (pass + 1 < PASSES) {
-            wg = ng;
-            wu = nu;
-            row_local = next_local;
-        }
+        wg0 = wg1;
+        wu0 = wu1;
+        wg1 = ng;
+        wu1 = nu;
     }
     if constexpr (QUANT) {
         __syncthreads();

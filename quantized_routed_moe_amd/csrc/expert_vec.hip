@@ -19,66 +19,74 @@ template <int K, int FMT, bool DUMP, bool SKIP_SHARED>
 __global__ __launch_bounds__(256) void gateup_vec_kernel(LayerArgs a) {
     __shared__ VecSmem<K, kVecTok> sm;
     const int g = blockIdx.y;
-    if (g >= a.ws.ctl[kCtlGroups]) return;
-    const int4 grp = a.ws.groups[g];
+    const int ngroups = a.ws.ctl[kCtlGroups];
+    const int4 grp = a.ws.groups[g];  // in the allocation for every g of the grid; used only when g < ngroups
+    if (g >= ngroups) return;
     const bool shared = grp.x == a.d.E;
     if (SKIP_SHARED && shared) return;
     const int tid = threadIdx.x;
-    if (tid < grp.z) {
-        const int p = shared ? a.d.T * a.d.k + grp.y + tid : a.ws.perm[grp.y + tid];
-        sm.pair[tid] = p;
-        sm.row[tid] = shared ? grp.y + tid : p / a.d.k;
-    }
-    __syncthreads();
     const int r0 = blockIdx.x * kVecRows;
+    // the group's pairs are requested before the weight rows (a wave waits for
+    // loads in issue order); their x rows are staged while the rows stream in
+    int p = 0;
+    if (tid < grp.z) p = shared ? a.d.T * a.d.k + grp.y + tid : a.ws.perm[grp.y + tid];
+    auto stage = [&](bool s16) {
+        if (tid < grp.z) {
+            sm.pair[tid] = p;
+            sm.row[tid] = shared ? grp.y + tid : p / a.d.k;
+        }
+        __syncthreads();
+        if (s16) stage_rows<K, kVecTok, true>(sm, a.ws.xq, a.ws.xd, a.ws.xs16, grp.z);
+        else stage_rows<K, kVecTok, false>(sm, a.ws.xq, a.ws.xd, nullptr, grp.z);
+        __syncthreads();
+    };
     if (shared) {
-        stage_rows<K, kVecTok, false>(sm, a.ws.xq, a.ws.xd, nullptr, grp.z);
-        __syncthreads();
-        gateup_rows<K, kFmtQ8, kVecTok, kVecRows, true, DUMP>(a, sm, a.wt.sh_gate, a.wt.sh_up, grp.z, r0);
+        gateup_rows<K, kFmtQ8, kVecTok, kVecRows, true, DUMP>(a, sm, a.wt.sh_gate, a.wt.sh_up, grp.z, r0,
+                                                             [&] { stage(false); });
     } else {
-        stage_rows<K, kVecTok, FMT == kFmtQ2>(sm, a.ws.xq, a.ws.xd, a.ws.xs16, grp.z);
-        __syncthreads();
         const int64_t mb = mat_bytes(FMT, a.d.F, K);
         gateup_rows<K, FMT, kVecTok, kVecRows, true, DUMP>(a, sm, a.wt.gate + grp.x * mb, a.wt.up + grp.x * mb, grp.z,
-                                                          r0);
+                                                          r0, [&] { stage(FMT == kFmtQ2); });
     }
 }
 
 // y[p][r] = w_p * (down row r . h_p) for rows r0..r0+31 of one expert.  The
 // lane geometry L is the routed format's for every expert (the shared Q8
 // expert included), the same one the one-token down kernel uses, so a token's
-// y values do not depend on the batch it is served in.
-template <int K, int FMT, int L, bool DUMP>
+// y values do not depend on the batch it is served in.  Rows of the next two
+// passes stay in flight; the first two are requested before `stage()` (the
+// caller's staging of h, ending with a barrier).
+template <int K, int FMT, int L, bool DUMP, class Stage>
 __device__ void down_rows(const LayerArgs &a, VecSmem<K, kVecTok> &sm, const uint8_t *__restrict__ dmat, int cnt,
-                          int r0) {
+                          int r0, Stage stage) {
     using G = Geo<K, FMT, L>;
+    using RR = RowRegs<K, FMT, G::L>;
     constexpr int PASSES = kVecRows / (4 * G::RPW);
     static_assert(PASSES >= 1 && kVecRows % (4 * G::RPW) == 0, "row geometry");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const Dims &d = a.d;
     const int seg = lane % G::L, rsub = lane / G::L;
-    RowRegs<K, FMT, G::L> wr;
-    int row_local = wave * G::RPW + rsub;
-    wr.load(dmat, d.H, r0 + row_local, seg);
-#pragma unroll 1
+    auto row_of = [&](int pass) { return (pass * 4 + wave) * G::RPW + rsub; };
+    RR w0, w1;
+    w0.load(dmat, d.H, r0 + row_of(0), seg);
+    if (PASSES > 1) w1.load(dmat, d.H, r0 + row_of(1), seg);
+    stage();
+#pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-        RowRegs<K, FMT, G::L> nr;
-        const int next_local = ((pass + 1) * 4 + wave) * G::RPW + rsub;
-        if (pass + 1 < PASSES) nr.load(dmat, d.H, r0 + next_local, seg);
-        const int r = r0 + row_local;
+        RR nw;
+        if (pass + 2 < PASSES) nw.load(dmat, d.H, r0 + row_of(pass + 2), seg);
+        const int r = r0 + row_of(pass);
         const bool dump_row = DUMP && (r % a.dump.stride == 0);
         for (int tok = 0; tok < cnt; ++tok) {
             int32_t *dd = nullptr;
             if (dump_row)
                 dd = a.dump.down_sums +
                      ((int64_t)sm.pair[tok] * (d.H / a.dump.stride) + r / a.dump.stride) * a.dump.pitch_dn;
-            const float y = group_sum<G::L>(lane_dot<K, G::L>(wr, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dd));
+            const float y = group_sum<G::L>(lane_dot<K, G::L>(w0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dd));
             if (seg == 0) a.ws.y[(int64_t)sm.pair[tok] * d.H + r] = __fmul_rn(sm.w[tok], y);
         }
-        if (pass + 1 < PASSES) {
-            wr = nr;
-            row_local = next_local;
-        }
+        w0 = w1;
+        w1 = nw;
     }
 }
 
@@ -86,30 +94,37 @@ template <int K, int FMT, bool DUMP>
 __global__ __launch_bounds__(256) void down_vec_kernel(LayerArgs a) {
     __shared__ VecSmem<K, kVecTok> sm;
     const int g = blockIdx.y;
-    if (g >= a.ws.ctl[kCtlGroups]) return;
-    const int4 grp = a.ws.groups[g];
+    const int ngroups = a.ws.ctl[kCtlGroups];
+    const int4 grp = a.ws.groups[g];  // in the allocation for every g of the grid; used only when g < ngroups
+    if (g >= ngroups) return;
     const bool shared = grp.x == a.d.E;
     const int tid = threadIdx.x;
-    if (tid < grp.z) {
-        const int p = shared ? a.d.T * a.d.k + grp.y + tid : a.ws.perm[grp.y + tid];
-        sm.pair[tid] = p;
-        sm.row[tid] = p;  // h is stored per pair
-        sm.w[tid] = shared ? 1.0f : a.ws.w[p];
-    }
-    __syncthreads();
-    stage_rows<K, kVecTok, false>(sm, a.ws.hq, a.ws.hd, nullptr, grp.z);
-    __syncthreads();
     const int r0 = blockIdx.x * kVecRows;
     constexpr int L = DefLpr<K, FMT>::v;
-    if (shared) {
-        down_rows<K, kFmtQ8, L, DUMP>(a, sm, a.wt.sh_down, grp.z, r0);
-    } else {
-        if constexpr (FMT == kFmtQ2) {
+    // pairs and combine weights are requested before the weight rows
+    int p = 0;
+    if (tid < grp.z) p = shared ? a.d.T * a.d.k + grp.y + tid : a.ws.perm[grp.y + tid];
+    float wp = 1.0f;
+    if (tid < grp.z && !shared) wp = a.ws.w[p];
+    auto stage = [&](bool sums) {
+        if (tid < grp.z) {
+            sm.pair[tid] = p;
+            sm.row[tid] = p;  // h is stored per pair
+            sm.w[tid] = wp;
+        }
+        __syncthreads();
+        stage_rows<K, kVecTok, false>(sm, a.ws.hq, a.ws.hd, nullptr, grp.z);
+        __syncthreads();
+        if (sums) {
             subblock_sums(sm, grp.z);
             __syncthreads();
         }
+    };
+    if (shared) {
+        down_rows<K, kFmtQ8, L, DUMP>(a, sm, a.wt.sh_down, grp.z, r0, [&] { stage(false); });
+    } else {
         const int64_t mb = mat_bytes(FMT, a.d.H, K);
-        down_rows<K, FMT, L, DUMP>(a, sm, a.wt.down + grp.x * mb, grp.z, r0);
+        down_rows<K, FMT, L, DUMP>(a, sm, a.wt.down + grp.x * mb, grp.z, r0, [&] { stage(FMT == kFmtQ2); });
     }
 }
 
