@@ -68,6 +68,7 @@ KERNEL_SOURCES = {
     "decode_front_kernel": ["decode.hip", "dev_route.hpp", "dev_vec.hpp", "common.hpp"],
     "decode_select_kernel": ["decode.hip", "dev_route.hpp", "dev_vec.hpp", "common.hpp"],
     "decode_down1_kernel": ["decode.hip", "dev_route.hpp", "dev_vec.hpp", "common.hpp"],
+    "decode_gateup1_kernel": ["decode.hip", "dev_route.hpp", "dev_vec.hpp", "common.hpp"],
     "gateup_vec_kernel": ["expert_vec.hip", "dev_vec.hpp", "common.hpp"],
     "down_vec_kernel": ["expert_vec.hip", "dev_vec.hpp", "common.hpp"],
     "combine_kernel": ["expert_vec.hip", "dev_vec.hpp", "common.hpp"],
@@ -103,7 +104,8 @@ def stage_kernel(cfg, stage):
     """Name of the one kernel a stage launches on this workload's path."""
     T, mfma = cfg.tokens, (cfg.routed_fmt == "q8" and cfg.hidden >= 256 and cfg.ffn >= 256)
     if T <= 32:
-        return {"route": "decode_front_kernel", "select": "decode_select_kernel", "gateup": "gateup_vec_kernel",
+        return {"route": "decode_front_kernel", "select": "decode_select_kernel",
+                "gateup": "decode_gateup1_kernel" if T == 1 else "gateup_vec_kernel",
                 "down": "decode_down1_kernel" if T == 1 else "down_vec_kernel",
                 "combine": "combine_kernel"}.get(stage)
     return {"quant": "quant_kernel", "logits": "logits_tiled_kernel", "select": "select_kernel",
@@ -138,8 +140,12 @@ def stage_model(cfg, qr, u_avg):
     st = {}
     if T <= 32:
         st["route"] = router + x32 + xq + rout + sh * (2 * mq8_gu + T * F * 4)
-        st["select"] = (2 * T * E * 4 if learned else T * 4) + sh * (T * F * 4 + hq(T)) + T * k * 12
-        st["gateup"] = u_avg * 2 * mr_gu + xq + hq(Pr)
+        sel = (2 * T * E * 4 if learned else T * 4) + sh * (T * F * 4 + hq(T)) + T * k * 12
+        if T == 1:  # the selection and the shared h quantization run inside the gate/up kernel
+            st["gateup"] = u_avg * 2 * mr_gu + xq + hq(Pr) + sel
+        else:
+            st["select"] = sel
+            st["gateup"] = u_avg * 2 * mr_gu + xq + hq(Pr)
         if T == 1:
             st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + x32
         else:

@@ -195,11 +195,13 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
     a.group_tok = kVecTok;
     if (T <= kDecodeMaxT) {
         run(MOE_STAGE_ROUTE, [&] { return launch_decode_front(a, dump, s); });
-        run(MOE_STAGE_SELECT, [&] { return launch_decode_select(a, s); });
-        run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, true, dump, s); });
         if (T == 1) {
+            // one token: the selection runs inside the gate/up workgroups
+            run(MOE_STAGE_GATEUP, [&] { return launch_decode_gateup1(a, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_decode_down1(a, dump, s); });
         } else {
+            run(MOE_STAGE_SELECT, [&] { return launch_decode_select(a, s); });
+            run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, true, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
             run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
         }

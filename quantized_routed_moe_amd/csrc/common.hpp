@@ -247,6 +247,7 @@ hipError_t launch_ws_init(int32_t *ctl, int64_t n_words, hipStream_t s);
 hipError_t launch_decode_front(const LayerArgs &a, bool dump, hipStream_t s);
 hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s);
 hipError_t launch_select_sort(const LayerArgs &a, hipStream_t s);
+hipError_t launch_decode_gateup1(const LayerArgs &a, bool dump, hipStream_t s);
 hipError_t launch_decode_down1(const LayerArgs &a, bool dump, hipStream_t s);
 hipError_t launch_quant(const LayerArgs &a, hipStream_t s);
 hipError_t launch_logits(const LayerArgs &a, hipStream_t s);

@@ -189,6 +189,128 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
     }
 }
 
+// ---------------------------------------------------- gate/up, one token
+// T == 1: the selection is repeated in every workgroup instead of running in
+// a kernel of its own (it costs each workgroup about as much as its first
+// weight request, and saves a dependent launch).  blockIdx.y is the slot: the
+// position of the workgroup's expert among the distinct selected experts in
+// ascending id; the slot after the last routed one is the shared expert,
+// whose workgroups quantize one 32-row block of its h each (the front kernel
+// left it in fp32).  Workgroup (0, 0) publishes the routing for the down
+// kernel and the debug copies: ids and w in rank order, perm (pairs by
+// expert, then slot), counts, offsets and the work list.
+struct Sel1Smem {
+    int32_t ids[8];
+    float w[8];
+    int32_t pairs[8];  // rank slots ordered by (expert, slot)
+    int32_t uniq[8];   // distinct selected experts, ascending
+    int32_t first[8];  // position in `pairs` of each distinct expert's first pair
+    int32_t nuniq;
+    int32_t flags;     // hash-path flags of workgroups other than (0, 0)
+};
+
+constexpr int kG1Rows = 64;   // rows of one workgroup: two h blocks
+constexpr int kG1Waves = 8;
+
+template <int K, int FMT, bool DUMP>
+__global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
+    __shared__ VecSmem<K, kVecTok> sm;
+    __shared__ Sel1Smem ss;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Dims &d = a.d;
+    const int slot = blockIdx.y;
+    if (slot == d.k) {  // shared expert: quantize the two h blocks of this workgroup's rows (pair k)
+        if (tid < kG1Rows / 32)
+            quant_one_block(a.ws.h + (int64_t)d.k * d.F, a.ws.hq + (int64_t)d.k * d.F,
+                            a.ws.hd + (int64_t)d.k * (d.F / 32), nullptr, blockIdx.x * (kG1Rows / 32) + tid);
+        return;
+    }
+    const bool publish = blockIdx.x == 0 && slot == 0;
+    if (wave == 0) {
+        if (d.route == kRouteLearned)
+            select_keys_wave(a.ws.keys, a.ws.scores, d.E, d.k, ss.ids, ss.w, lane);
+        else
+            select_hash_wave(a.token_ids, a.wt.table, 0, d.vocab, d.E, d.k, ss.ids, ss.w,
+                             publish ? a.ws.ctl + kCtlFlags : &ss.flags, lane);
+    } else {
+        // meanwhile the token's quantized x goes to LDS slot 0
+        for (int i = tid - 64; i < K / 16; i += 64 * (kG1Waves - 1)) {
+            reinterpret_cast<int4 *>(sm.aq[0])[i] = reinterpret_cast<const int4 *>(a.ws.xq)[i];
+            if (i < K / 32) sm.ad[0][i] = a.ws.xd[i];
+            if (FMT == kFmtQ2) sm.as16[0][i] = a.ws.xs16[i];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // rank of each slot by (expert, slot); distinct experts in ascending id
+        const int k = d.k;
+        const int e = lane < k ? ss.ids[lane] : 0x7fffffff;
+        int rank = 0;
+        for (int i = 0; i < k; ++i) {
+            const int f = ss.ids[i];
+            rank += (f < e) || (f == e && i < lane);
+        }
+        if (lane < k) ss.pairs[rank] = lane;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const int j = lane < k ? ss.pairs[lane] : 0;
+        const int ej = lane < k ? ss.ids[j] : -1;
+        const int eprev = __shfl_up(ej, 1);
+        const bool is_first = lane < k && (lane == 0 || eprev != ej);
+        const uint64_t firsts = __ballot(is_first);
+        if (is_first) {
+            const int u = __popcll(firsts & ((1ull << lane) - 1ull));
+            ss.uniq[u] = ej;
+            ss.first[u] = lane;
+        }
+        if (lane == 0) ss.nuniq = __popcll(firsts);
+    }
+    __syncthreads();
+    const int nuniq = ss.nuniq;
+    if (publish) {
+        const int k = d.k;
+        if (tid < k) {
+            a.ws.ids[tid] = ss.ids[tid];
+            a.ws.w[tid] = ss.w[tid];
+            a.ws.perm[tid] = ss.pairs[tid];
+        }
+        for (int e = tid; e < d.E; e += 64 * kG1Waves) {
+            int c = 0, below = 0;
+            for (int i = 0; i < k; ++i) {
+                c += ss.ids[i] == e;
+                below += ss.ids[i] < e;
+            }
+            a.ws.counts[e] = c;
+            a.ws.offsets[e] = below;
+        }
+        if (tid < nuniq) {
+            const int f = ss.first[tid], n = (tid + 1 < nuniq ? ss.first[tid + 1] : k) - f;
+            a.ws.groups[tid] = make_int4(ss.uniq[tid], f, n, ss.pairs[f]);
+        }
+        if (tid == 0) {
+            a.ws.offsets[d.E] = k;
+            if (d.has_shared) a.ws.groups[nuniq] = make_int4(d.E, 0, 1, k);
+            a.ws.ctl[kCtlGroups] = nuniq + d.has_shared;
+        }
+    }
+    if (slot >= nuniq) return;  // fewer distinct experts than k (a repeated hash-table id)
+    const int e = ss.uniq[slot], f = ss.first[slot];
+    const int cnt = (slot + 1 < nuniq ? ss.first[slot + 1] : d.k) - f;
+    if (tid < cnt) {
+        sm.pair[tid] = ss.pairs[f + tid];
+        sm.row[tid] = 0;
+    }
+    // a repeated expert (cnt > 1) applies to the same x: copy slot 0
+    for (int i = tid; i < (cnt - 1) * (K / 16); i += 64 * kG1Waves) {
+        const int tok = 1 + i / (K / 16), c = i % (K / 16);
+        reinterpret_cast<int4 *>(sm.aq[tok])[c] = reinterpret_cast<const int4 *>(sm.aq[0])[c];
+        if (c < K / 32) sm.ad[tok][c] = sm.ad[0][c];
+        if (FMT == kFmtQ2) sm.as16[tok][c] = sm.as16[0][c];
+    }
+    const int64_t mb = mat_bytes(FMT, d.F, K);
+    gateup_rows<K, FMT, kVecTok, kG1Rows, true, DUMP, kG1Waves>(a, sm, a.wt.gate + e * mb, a.wt.up + e * mb, cnt,
+                                                               blockIdx.x * kG1Rows, [&] { __syncthreads(); });
+}
+
 // -------------------------------------------------------- down, one token
 // Rows of the output: each wave pass covers RPW rows (LPR lanes per row, the
 // routed format's geometry; the shared Q8 expert reuses it with more chunks
@@ -341,6 +463,27 @@ hipError_t launch_decode_front(const LayerArgs &a, bool dump, hipStream_t s) {
 hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s) {
     klaunch(decode_select_kernel, dim3(1), dim3(256), s, a);
     return hipGetLastError();
+}
+
+template <int FMT, bool DUMP>
+static hipError_t gateup1_f(const LayerArgs &a, hipStream_t s) {
+    const dim3 grid(a.d.F / kG1Rows, a.d.k + a.d.has_shared), block(64 * kG1Waves);
+    switch (a.d.H) {
+        case 128: if constexpr (FMT == kFmtQ8) { klaunch(decode_gateup1_kernel<128, FMT, DUMP>, grid, block, s, a); break; } return hipErrorInvalidValue;
+        case 256: if constexpr (FMT == kFmtQ8) { klaunch(decode_gateup1_kernel<256, FMT, DUMP>, grid, block, s, a); break; } return hipErrorInvalidValue;
+        case 512: klaunch(decode_gateup1_kernel<512, FMT, DUMP>, grid, block, s, a); break;
+        case 1024: klaunch(decode_gateup1_kernel<1024, FMT, DUMP>, grid, block, s, a); break;
+        case 2048: klaunch(decode_gateup1_kernel<2048, FMT, DUMP>, grid, block, s, a); break;
+        case 4096: klaunch(decode_gateup1_kernel<4096, FMT, DUMP>, grid, block, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gateup1(const LayerArgs &a, bool dump, hipStream_t s) {
+    if (a.d.T != 1) return hipErrorInvalidValue;
+    if (a.d.fmt == kFmtQ8) return dump ? gateup1_f<kFmtQ8, true>(a, s) : gateup1_f<kFmtQ8, false>(a, s);
+    return dump ? gateup1_f<kFmtQ2, true>(a, s) : gateup1_f<kFmtQ2, false>(a, s);
 }
 
 template <int F, int FMT, bool DUMP>

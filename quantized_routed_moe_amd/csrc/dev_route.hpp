@@ -91,18 +91,28 @@ __device__ __forceinline__ uint32_t key_order(float key) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Maximum of v over the wave, returned uniform: a prefix maximum inside each
+// 16-lane row (DPP row shifts by 1, 2, 4, 8; a lane without a source keeps 0),
+// then the maxima of the four rows' last lanes.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 // One wave selects the top-k (k <= 8 <= E) experts of one token from its keys
 // (larger key first, equal keys: smaller expert id) and weights them by
-// score / sum of the selected scores, summed in rank order.
-//  1. tau = the k-th largest key image, found bit by bit from the top: a bit
-//     is kept when at least k keys are >= the threshold with it set (ballot
-//     counts, uniform scalar work).
-//  2. selected = keys above tau, then keys equal to tau in ascending expert id
-//     until k are taken.
-//  3. each selected expert's rank = number of keys ordered before it; lane
-//     `rank` keeps its id and score, lanes 0..k-1 write the result.
-//  PER candidate slots per lane (64 * PER >= E); slots past E sort below
-//  every key and are never counted or selected.
+// score / sum of the selected scores, summed in rank order.  k rounds: the
+// wave maximum of the remaining key images, the smallest expert id holding
+// it (one ballot per candidate slot, slots in id order), which is then
+// removed.  Lane `rank` keeps the id and score of that rank; lanes 0..k-1
+// write the result.
+//  PER candidate slots per lane (64 * PER >= E); slots past E hold 0, below
+//  every key image, and are never taken.
 template <int PER>
 __device__ void select_keys_per(const float *__restrict__ krow, const float *__restrict__ srow, int E, int k,
                                 int32_t *ids_out, float *w_out, int lane) {
@@ -112,60 +122,39 @@ __device__ void select_keys_per(const float *__restrict__ krow, const float *__r
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
         const bool ok = e < E;
-        u[i] = ok ? key_order(krow[e]) : 0u;  // absent candidates sort below every key
+        u[i] = ok ? key_order(krow[e]) : 0u;
         s[i] = ok ? srow[e] : 0.0f;
     }
-    uint32_t tau = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = tau | (1u << bit);
-        int n = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            n += __popcll(__ballot(u[i] >= c));
-        if (n >= k) tau = c;
-    }
-    uint64_t selb[PER];
-    int need = k;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        selb[i] = __ballot(u[i] > tau);
-        need -= __popcll(selb[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        uint64_t eq = __ballot(u[i] == tau);
-        while (eq && need > 0) {  // lowest lane = smallest id within the slot
-            const uint64_t low = eq & (~eq + 1ull);
-            selb[i] |= low;
-            eq ^= low;
-            --need;
-        }
-    }
     int my_id = 0;
-    float my_s = 0.0f;
+    float my_s = 0.0f, S = 0.0f;
+    for (int r = 0; r < k; ++r) {
+        uint32_t lm = u[0];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        uint64_t m = selb[i];
-        while (m) {
-            const int l = __builtin_ctzll(m);
-            m &= m - 1;
-            const uint32_t ux = __builtin_amdgcn_readlane(u[i], l);
-            const float sx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[i]), l));
-            const int ex = l + 64 * i;
-            int rank = 0;
+        for (int i = 1; i < PER; ++i) lm = max(lm, u[i]);
+        const uint32_t m = wave_max_u32(lm);
+        // smallest id holding m: the first slot (ids lane + 64*i) with a match, its lowest lane
+        int slot = -1, owner = 0;
 #pragma unroll
-            for (int j = 0; j < PER; ++j)
-                rank += __popcll(__ballot(u[j] > ux || (u[j] == ux && lane + 64 * j < ex)));
-            if (lane == rank) {
-                my_id = ex;
-                my_s = sx;
+        for (int i = 0; i < PER; ++i) {
+            const uint64_t b = __ballot(u[i] == m);
+            if (slot < 0 && b != 0ull) {
+                slot = i;
+                owner = __builtin_ctzll(b);
             }
         }
-    }
-    float S = 0.0f;
+        float sx = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < k) S += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
+        for (int i = 0; i < PER; ++i)
+            if (i == slot) {
+                sx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[i]), owner));
+                if (lane == owner) u[i] = 0u;
+            }
+        S += sx;
+        if (lane == r) {
+            my_id = owner + 64 * slot;
+            my_s = sx;
+        }
+    }
     if (lane < k) {
         ids_out[lane] = my_id;
         w_out[lane] = my_s / S;

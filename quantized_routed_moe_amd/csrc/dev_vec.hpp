@@ -14,7 +14,7 @@ struct VecSmem {
     alignas(16) int8_t aq[NTOK][K];
     float ad[NTOK][K / 32];
     int32_t as16[NTOK][K / 16];
-    float h[NTOK][kVecRows];
+    float h[NTOK][2 * kVecRows];  // up to 64 rows of h per workgroup
     int32_t pair[NTOK];
     int32_t row[NTOK];
     float w[NTOK];
@@ -194,17 +194,20 @@ struct GuRows {
 // are requested before `stage()` runs (the caller's activation staging, which
 // ends with a barrier), so weight streaming starts as soon as the expert is
 // known.
-template <int K, int FMT, int NTOK, int ROWS, bool QUANT, bool DUMP, class Stage>
+// NW waves per workgroup; with QUANT the workgroup's NW*64 threads cover
+// NTOK tokens x ROWS rows of h (ROWS a multiple of the 32-row h block).
+template <int K, int FMT, int NTOK, int ROWS, bool QUANT, bool DUMP, int NW = 4, class Stage>
 __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint8_t *__restrict__ gmat,
                             const uint8_t *__restrict__ umat, int cnt, int r0, Stage stage) {
     using G = Geo<K, FMT>;
     using RR = RowRegs<K, FMT, G::L>;
-    constexpr int PASSES = ROWS / (4 * G::RPW);
-    static_assert(PASSES >= 1 && ROWS % (4 * G::RPW) == 0 && (!QUANT || ROWS == kVecRows), "row geometry");
+    constexpr int PASSES = ROWS / (NW * G::RPW);
+    static_assert(PASSES >= 1 && ROWS % (NW * G::RPW) == 0, "row geometry");
+    static_assert(!QUANT || (ROWS % kVecRows == 0 && ROWS <= 2 * kVecRows && NW * 64 == NTOK * ROWS), "h blocks");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int seg = lane % G::L, rsub = lane / G::L;
-    auto row_of = [&](int pass) { return (pass * 4 + wave) * G::RPW + rsub; };
+    auto row_of = [&](int pass) { return (pass * NW + wave) * G::RPW + rsub; };
     RR wg0, wu0, wg1, wu1;
     wg0.load(gmat, d.F, r0 + row_of(0), seg);
     wu0.load(umat, d.F, r0 + row_of(0), seg);
@@ -248,7 +251,7 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
     }
     if constexpr (QUANT) {
         __syncthreads();
-        const int tok = tid >> 5, i = tid & 31;
+        const int tok = tid / ROWS, i = tid % ROWS;  // 32 consecutive lanes = one h block of one token
         const float v = tok < cnt ? sm.h[tok][i] : 0.0f;
         const float amax = group_max<32>(fabsf(v));
         if (tok < cnt) {
@@ -256,7 +259,7 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
             const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
             const int p = sm.pair[tok];
             a.ws.hq[(int64_t)p * d.F + r0 + i] = (int8_t)quant_code(v, inv);
-            if (i == 0) a.ws.hd[(int64_t)p * (d.F / 32) + r0 / 32] = dsc;
+            if (i % 32 == 0) a.ws.hd[(int64_t)p * (d.F / 32) + (r0 + i) / 32] = dsc;
         }
     }
 }
