@@ -139,11 +139,13 @@ def stage_model(cfg, qr, u_avg):
     rout = 3 * T * E * 4 if learned else 0
     st = {}
     if T <= 32:
-        st["route"] = router + x32 + xq + rout + sh * (2 * mq8_gu + T * F * 4)
-        sel = (2 * T * E * 4 if learned else T * 4) + sh * (T * F * 4 + hq(T)) + T * k * 12
-        if T == 1:  # the selection and the shared h quantization run inside the gate/up kernel
-            st["gateup"] = u_avg * 2 * mr_gu + xq + hq(Pr) + sel
+        sel = (2 * T * E * 4 if learned else T * 4) + T * k * 12
+        if T == 1:  # selection and the shared expert's gate/up run in the gate/up kernel
+            st["route"] = router + x32 + xq + rout
+            st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P) + sel
         else:
+            st["route"] = router + x32 + xq + rout + sh * (2 * mq8_gu + T * F * 4)
+            sel += sh * (T * F * 4 + hq(T))
             st["select"] = sel
             st["gateup"] = u_avg * 2 * mr_gu + xq + hq(Pr)
         if T == 1:

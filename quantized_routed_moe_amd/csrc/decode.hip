@@ -2,9 +2,9 @@
 //
 //  front   quantize x and compute the router logits, scores and selection
 //          keys (learned layers: one workgroup per logit, the four waves each
-//          sum a quarter of the adjacent-pair tree), while further workgroups
-//          stream the shared expert's gate/up rows, which need no routing,
-//          leaving its h in fp32.
+//          sum a quarter of the adjacent-pair tree); for 2..32 tokens further
+//          workgroups stream the shared expert's gate/up rows, which need no
+//          routing, leaving its h in fp32.
 //  select  one workgroup: top-k or hash selection, sort, work list, and the
 //          quantization of the shared expert's h.
 //  gateup  routed experts' gate/up + SwiGLU + h quantization (expert_vec.hip).
@@ -195,8 +195,8 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
 // weight request, and saves a dependent launch).  blockIdx.y is the slot: the
 // position of the workgroup's expert among the distinct selected experts in
 // ascending id; the slot after the last routed one is the shared expert,
-// whose workgroups quantize one 32-row block of its h each (the front kernel
-// left it in fp32).  Workgroup (0, 0) publishes the routing for the down
+// whose gate/up rows stream from the start (the front kernel computes only
+// the router for one token).  Workgroup (0, 0) publishes the routing for the down
 // kernel and the debug copies: ids and w in rank order, perm (pairs by
 // expert, then slot), counts, offsets and the work list.
 struct Sel1Smem {
@@ -219,10 +219,19 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int slot = blockIdx.y;
-    if (slot == d.k) {  // shared expert: quantize the two h blocks of this workgroup's rows (pair k)
-        if (tid < kG1Rows / 32)
-            quant_one_block(a.ws.h + (int64_t)d.k * d.F, a.ws.hq + (int64_t)d.k * d.F,
-                            a.ws.hd + (int64_t)d.k * (d.F / 32), nullptr, blockIdx.x * (kG1Rows / 32) + tid);
+    if (slot == d.k) {  // shared expert (pair k): needs no routing, streams while the others select
+        if (tid == 0) {
+            sm.pair[0] = d.k;
+            sm.row[0] = 0;
+        }
+        gateup_rows<K, kFmtQ8, kVecTok, kG1Rows, true, DUMP, kG1Waves>(
+            a, sm, a.wt.sh_gate, a.wt.sh_up, 1, blockIdx.x * kG1Rows, [&] {
+                for (int i = tid; i < K / 16; i += 64 * kG1Waves) {
+                    reinterpret_cast<int4 *>(sm.aq[0])[i] = reinterpret_cast<const int4 *>(a.ws.xq)[i];
+                    if (i < K / 32) sm.ad[0][i] = a.ws.xd[i];
+                }
+                __syncthreads();
+            });
         return;
     }
     const bool publish = blockIdx.x == 0 && slot == 0;
@@ -443,7 +452,8 @@ static hipError_t front_h(const LayerArgs &a, hipStream_t s) {
         n_lead = nl > nq ? nl : nq;
     }
     if (n_lead > 4096) n_lead = 4096;
-    const int ns = d.has_shared ? (d.F / GuRows<H, kFmtQ8>::v) * ((d.T + kVecTok - 1) / kVecTok) : 0;
+    // one token: the shared expert's gate/up runs in the one-token gate/up kernel instead
+    const int ns = d.has_shared && d.T > 1 ? (d.F / GuRows<H, kFmtQ8>::v) * ((d.T + kVecTok - 1) / kVecTok) : 0;
     klaunch(decode_front_kernel<H, DUMP>, dim3(n_lead + ns), dim3(256), s, a, n_lead);
     return hipGetLastError();
 }
