@@ -236,11 +236,43 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
     }
     const bool publish = blockIdx.x == 0 && slot == 0;
     if (wave == 0) {
+        int id;
+        float w;
         if (d.route == kRouteLearned)
-            select_keys_wave(a.ws.keys, a.ws.scores, d.E, d.k, ss.ids, ss.w, lane);
+            select_keys_regs(a.ws.keys, a.ws.scores, d.E, d.k, id, w, lane);
         else
-            select_hash_wave(a.token_ids, a.wt.table, 0, d.vocab, d.E, d.k, ss.ids, ss.w,
+            select_hash_regs(a.token_ids, a.wt.table, 0, d.vocab, d.E, d.k, id, w,
                              publish ? a.ws.ctl + kCtlFlags : &ss.flags, lane);
+        // lane j < k holds rank slot j: order the slots by (expert, slot) in
+        // registers, then the distinct experts in ascending id
+        const int k = d.k;
+        const int e = lane < k ? id : 0x7fffffff;
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < k) {
+                const int f = __builtin_amdgcn_readlane(e, i);
+                rank += (f < e) || (f == e && i < lane);
+            }
+        int src = 0;  // slot at sorted position `lane`
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k && __builtin_amdgcn_readlane(rank, j) == lane) src = j;
+        const int ej = __shfl(e, src);
+        const int eprev = __shfl_up(ej, 1);
+        const bool is_first = lane < k && (lane == 0 || eprev != ej);
+        const uint64_t firsts = __ballot(is_first);
+        if (lane < k) {
+            ss.ids[lane] = id;
+            ss.w[lane] = w;
+            ss.pairs[lane] = src;
+        }
+        if (is_first) {
+            const int u = __popcll(firsts & ((1ull << lane) - 1ull));
+            ss.uniq[u] = ej;
+            ss.first[u] = lane;
+        }
+        if (lane == 0) ss.nuniq = __popcll(firsts);
     } else {
         // meanwhile the token's quantized x goes to LDS slot 0
         for (int i = tid - 64; i < K / 16; i += 64 * (kG1Waves - 1)) {
@@ -248,30 +280,6 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
             if (i < K / 32) sm.ad[0][i] = a.ws.xd[i];
             if (FMT == kFmtQ2) sm.as16[0][i] = a.ws.xs16[i];
         }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        // rank of each slot by (expert, slot); distinct experts in ascending id
-        const int k = d.k;
-        const int e = lane < k ? ss.ids[lane] : 0x7fffffff;
-        int rank = 0;
-        for (int i = 0; i < k; ++i) {
-            const int f = ss.ids[i];
-            rank += (f < e) || (f == e && i < lane);
-        }
-        if (lane < k) ss.pairs[rank] = lane;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        const int j = lane < k ? ss.pairs[lane] : 0;
-        const int ej = lane < k ? ss.ids[j] : -1;
-        const int eprev = __shfl_up(ej, 1);
-        const bool is_first = lane < k && (lane == 0 || eprev != ej);
-        const uint64_t firsts = __ballot(is_first);
-        if (is_first) {
-            const int u = __popcll(firsts & ((1ull << lane) - 1ull));
-            ss.uniq[u] = ej;
-            ss.first[u] = lane;
-        }
-        if (lane == 0) ss.nuniq = __popcll(firsts);
     }
     __syncthreads();
     const int nuniq = ss.nuniq;

@@ -115,7 +115,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 //  every key image, and are never taken.
 template <int PER>
 __device__ void select_keys_per(const float *__restrict__ krow, const float *__restrict__ srow, int E, int k,
-                                int32_t *ids_out, float *w_out, int lane) {
+                                int &my_id, float &my_w, int lane) {
     uint32_t u[PER];
     float s[PER];
 #pragma unroll
@@ -125,7 +125,7 @@ __device__ void select_keys_per(const float *__restrict__ krow, const float *__r
         u[i] = ok ? key_order(krow[e]) : 0u;
         s[i] = ok ? srow[e] : 0.0f;
     }
-    int my_id = 0;
+    my_id = 0;
     float my_s = 0.0f, S = 0.0f;
     for (int r = 0; r < k; ++r) {
         uint32_t lm = u[0];
@@ -155,36 +155,60 @@ __device__ void select_keys_per(const float *__restrict__ krow, const float *__r
             my_s = sx;
         }
     }
-    if (lane < k) {
-        ids_out[lane] = my_id;
-        w_out[lane] = my_s / S;
-    }
+    my_w = my_s / S;
+}
+
+// Lane r < k of the calling wave receives the rank-r expert id and weight.
+__device__ __forceinline__ void select_keys_regs(const float *__restrict__ krow, const float *__restrict__ srow, int E,
+                                                 int k, int &id, float &w, int lane) {
+    if (E <= 64) select_keys_per<1>(krow, srow, E, k, id, w, lane);
+    else if (E <= 128) select_keys_per<2>(krow, srow, E, k, id, w, lane);
+    else if (E <= 256) select_keys_per<4>(krow, srow, E, k, id, w, lane);
+    else if (E <= 512) select_keys_per<8>(krow, srow, E, k, id, w, lane);
+    else select_keys_per<16>(krow, srow, E, k, id, w, lane);
 }
 
 __device__ __forceinline__ void select_keys_wave(const float *__restrict__ krow, const float *__restrict__ srow, int E,
                                                  int k, int32_t *ids_out, float *w_out, int lane) {
-    if (E <= 64) select_keys_per<1>(krow, srow, E, k, ids_out, w_out, lane);
-    else if (E <= 128) select_keys_per<2>(krow, srow, E, k, ids_out, w_out, lane);
-    else if (E <= 256) select_keys_per<4>(krow, srow, E, k, ids_out, w_out, lane);
-    else if (E <= 512) select_keys_per<8>(krow, srow, E, k, ids_out, w_out, lane);
-    else select_keys_per<16>(krow, srow, E, k, ids_out, w_out, lane);
+    int id;
+    float w;
+    select_keys_regs(krow, srow, E, k, id, w, lane);
+    if (lane < k) {
+        ids_out[lane] = id;
+        w_out[lane] = w;
+    }
 }
 
-__device__ void select_hash_wave(const int32_t *__restrict__ token_ids, const int32_t *__restrict__ table, int t,
-                                 int vocab, int E, int k, int32_t *ids_out, float *w_out, int32_t *flags, int lane) {
+// Lane j < k receives the token's j-th table entry (clamped and flagged when out of range) and 1/k.
+__device__ __forceinline__ void select_hash_regs(const int32_t *__restrict__ token_ids, const int32_t *__restrict__ table,
+                                                 int t, int vocab, int E, int k, int &id_out, float &w_out,
+                                                 int32_t *flags, int lane) {
     int id = token_ids[t];
     if (id < 0 || id >= vocab) {
         if (lane == 0) atomicOr(flags, 1);
         id = 0;
     }
+    id_out = 0;
+    w_out = 0.0f;
     if (lane < k) {
         int e = table[(int64_t)id * k + lane];
         if (e < 0 || e >= E) {
             atomicOr(flags, 2);
             e = 0;
         }
-        ids_out[lane] = e;
-        w_out[lane] = 1.0f / (float)k;
+        id_out = e;
+        w_out = 1.0f / (float)k;
+    }
+}
+
+__device__ void select_hash_wave(const int32_t *__restrict__ token_ids, const int32_t *__restrict__ table, int t,
+                                 int vocab, int E, int k, int32_t *ids_out, float *w_out, int32_t *flags, int lane) {
+    int id;
+    float w;
+    select_hash_regs(token_ids, table, t, vocab, E, k, id, w, flags, lane);
+    if (lane < k) {
+        ids_out[lane] = id;
+        w_out[lane] = w;
     }
 }
 
