@@ -17,14 +17,20 @@
 // takes A[j][l%32] and B[j][l%32] with j = l/32 and puts product j in
 // registers [16j, 16j+16) with the same row/column mapping.
 //
-// Workgroup: 4 waves as 2 (pairs) x 2 (columns), each wave 32 x 32; tile =
-// 64 pairs x 64 columns.  K runs in chunks of 4 blocks staged in LDS (padded
-// rows), the next chunk's global loads held in registers meanwhile.
+// Tile = 64 pairs x 64 columns.  K runs in chunks of 4 blocks staged in LDS
+// (padded rows), the next chunk's global loads held in registers meanwhile.
+// The scale products of two consecutive blocks come from one 2-block outer
+// product (lanes 0..31 supply block b, lanes 32..63 block b+1).
 //
-//  gate/up  B = 64 gate rows + 64 up rows; epilogue SwiGLU and the per-32
-//           column quantization of h (a wave's 32 columns = one block).
-//  down     B = 64 down rows (output rows); y = w_pair * acc, combined
+//  gate/up  8 waves: (gate | up) x 2 (pairs) x 2 (columns), each wave one
+//           32 x 32 tile of one matrix (fewer registers per wave, so more
+//           waves hide the epilogue's latency); after K, the up waves pass
+//           their sums through LDS and the gate waves apply SwiGLU and the
+//           per-32-column quantization of h (a wave's 32 columns = one block).
+//  down     4 waves: 2 (pairs) x 2 (output rows); y = w_pair * acc, combined
 //           afterwards in ascending expert id by the combine kernel.
+#include <utility>
+
 #include "dev_vec.hpp"
 
 namespace qrmoe {
@@ -42,6 +48,7 @@ struct GemmSmem {
     alignas(16) int8_t A[kTM][kRowB];    // activation codes of the chunk
     alignas(16) int8_t B[NBR][kRowB];    // weight codes of the chunk
     float sa[kKC][kTM];                  // activation block scales of the chunk
+    uint32_t sw[NBR][kKC / 2];           // weight block scales of the chunk (fp16 pairs)
     int32_t arow[kTM];                   // activation row of each tile row
     int32_t pair[kTM];
     float w[kTM];
@@ -53,14 +60,69 @@ __device__ __forceinline__ i32x4 g16nt(const void *p) {
 }
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-// Staging registers of one K chunk: 2 activation and NBR/32 weight 16-byte
-// pieces plus one activation scale per thread.
-template <int NBR>
+// Staging of one K chunk by NT threads: 16-byte activation and weight code
+// pieces, one activation block scale (threads < kKC * kTM) and one pair of
+// fp16 weight block scales (threads < 2 * NBR).  The global addresses of a
+// thread's pieces do not change from chunk to chunk and are set up once; the
+// compute phase reads only LDS, so no value loaded for a later chunk is
+// waited for early (a wave waits for its loads in issue order).
+template <int NT, int NBR>
 struct Stage {
-    static constexpr int NW = NBR * 8 / 256;
-    i32x4 a[2];
+    static constexpr int NA = kTM * 8 / NT;
+    static constexpr int NW = NBR * 8 / NT;
+    const int8_t *pa[NA];
+    const uint8_t *pb[NW];
+    const float *ps;
+    const uint32_t *pw;
+    i32x4 a[NA];
     i32x4 b[NW];
     float s;
+    uint32_t w;
+
+    // bmat(j): weight matrix of B staging row j; brow0(j): its first row index
+    template <int K, class BRow>
+    __device__ __forceinline__ void setup(const GemmSmem<NBR> &sm, const int8_t *__restrict__ act,
+                                          const float *__restrict__ ascale, int64_t R, BRow brow) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            pa[i] = act + (int64_t)sm.arow[row] * K + piece * 16;
+        }
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            pb[i] = brow(row).first + (int64_t)brow(row).second * K + piece * 16;
+        }
+        const int m = tid & 63, kb = (tid >> 6) & (kKC - 1);
+        ps = ascale + (int64_t)sm.arow[m] * (K / 32) + kb;
+        const int wr = (tid >> 1) % NBR, wh = tid & 1;
+        pw = reinterpret_cast<const uint32_t *>(brow(wr).first + R * K) + ((int64_t)brow(wr).second * (K / 32)) / 2 + wh;
+    }
+    __device__ __forceinline__ void load(int c) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) a[i] = g16(pa[i] + c * (kKC * 32));
+#pragma unroll
+        for (int i = 0; i < NW; ++i) b[i] = g16nt(pb[i] + c * (kKC * 32));
+        if (tid < kKC * kTM) s = ps[c * kKC];
+        if (tid < 2 * NBR) w = pw[c * (kKC / 2)];
+    }
+    __device__ __forceinline__ void store(GemmSmem<NBR> &sm) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            *reinterpret_cast<i32x4 *>(&sm.A[row][piece * 16]) = a[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            *reinterpret_cast<i32x4 *>(&sm.B[row][piece * 16]) = b[i];
+        }
+        if (tid < kKC * kTM) sm.sa[tid >> 6][tid & 63] = s;
+        if (tid < 2 * NBR) sm.sw[tid >> 1][tid & 1] = w;
+    }
 };
 
 // Tile setup: pairs, activation rows (token for x, pair for h) and weights.
@@ -79,57 +141,17 @@ __device__ __forceinline__ void setup_tile(const LayerArgs &a, GemmSmem<NBR> &sm
     __syncthreads();
 }
 
-// Global -> registers for chunk c.  brow(j) gives the weight row pointer of B
-// staging row j (0..NBR-1).
-template <int K, int NBR, class BRow>
-__device__ __forceinline__ void load_chunk(Stage<NBR> &st, const GemmSmem<NBR> &sm, const int8_t *__restrict__ act,
-                                           const float *__restrict__ ascale, BRow brow, int c) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 3, piece = idx & 7;
-        st.a[i] = g16(act + (int64_t)sm.arow[row] * K + c * (kKC * 32) + piece * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < Stage<NBR>::NW; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 3, piece = idx & 7;
-        st.b[i] = g16nt(brow(row) + c * (kKC * 32) + piece * 16);
-    }
-    {
-        const int kb = tid >> 6, m = tid & 63;
-        st.s = ascale[(int64_t)sm.arow[m] * (K / 32) + c * kKC + kb];
-    }
-}
-
+// fp16 weight scale of block kb (0..kKC-1) of staged weight row r
 template <int NBR>
-__device__ __forceinline__ void store_chunk(GemmSmem<NBR> &sm, const Stage<NBR> &st) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 3, piece = idx & 7;
-        *reinterpret_cast<i32x4 *>(&sm.A[row][piece * 16]) = st.a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Stage<NBR>::NW; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 3, piece = idx & 7;
-        *reinterpret_cast<i32x4 *>(&sm.B[row][piece * 16]) = st.b[i];
-    }
-    sm.sa[tid >> 6][tid & 63] = st.s;
-}
-
-// Weight block scales of one chunk for this lane's weight row: 4 fp16.
-__device__ __forceinline__ uint2 chunk_scales(const uint16_t *srow, int c) {
-    return *reinterpret_cast<const uint2 *>(srow + c * kKC);
-}
-__device__ __forceinline__ float scale_of(uint2 v, int kb) {
-    const uint32_t word = kb < 2 ? v.x : v.y;
-    return f16_to_f32((uint16_t)((kb & 1) ? (word >> 16) : (word & 0xffff)));
+__device__ __forceinline__ float wscale(const GemmSmem<NBR> &sm, int r, int kb) {
+    const uint32_t v = sm.sw[r][kb >> 1];
+    return f16_to_f32((uint16_t)((kb & 1) ? (v >> 16) : (v & 0xffff)));
 }
 
 // ------------------------------------------------------------- gate / up
 template <int H, bool DUMP>
-__global__ __launch_bounds__(256) void gateup_mfma_kernel(LayerArgs a) {
-    constexpr int NB = H / 32, NC = NB / kKC, NBR = 2 * kTN;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gateup_mfma_kernel(LayerArgs a) {
+    constexpr int NT = 512, NB = H / 32, NC = NB / kKC, NBR = 2 * kTN;
     __shared__ GemmSmem<NBR> sm;
     const int g = blockIdx.y;
     if (g >= a.ws.ctl[kCtlGroups]) return;
@@ -137,78 +159,80 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(LayerArgs a) {
     const bool shared = grp.x == a.d.E;
     const Dims &d = a.d;
     setup_tile(a, sm, grp, shared, false);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, n = lane & 31;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, n = lane & 31;
+    const int which = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;  // which: 0 gate, 1 up
     const uint8_t *gmat = shared ? a.wt.sh_gate : a.wt.gate + grp.x * q8_bytes(d.F, H);
     const uint8_t *umat = shared ? a.wt.sh_up : a.wt.up + grp.x * q8_bytes(d.F, H);
     const int c0 = blockIdx.x * kTN;
-    auto brow = [&](int j) -> const uint8_t * {
-        return j < kTN ? gmat + (int64_t)(c0 + j) * H : umat + (int64_t)(c0 + j - kTN) * H;
+    auto brow = [&](int j) {
+        return j < kTN ? std::make_pair(gmat, c0 + j) : std::make_pair(umat, c0 + j - kTN);
     };
     const int col = c0 + wn * 32 + n;  // this lane's h column (gate/up row)
-    // outer-product operand B: lanes 0..31 the gate scales, 32..63 the up scales of column col
-    const uint16_t *srow = reinterpret_cast<const uint16_t *>((half ? umat : gmat) + (int64_t)d.F * H) +
-                           (int64_t)col * NB;
-    float accg[16], accu[16];
+    const int brow_lds = which * kTN + wn * 32 + n;
+    float acc[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) accg[i] = accu[i] = 0.0f;
-    Stage<NBR> st;
-    load_chunk<H>(st, sm, a.ws.xq, a.ws.xd, brow, 0);
-    uint2 wnext = chunk_scales(srow, 0);
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    Stage<NT, NBR> st;
+    st.template setup<H>(sm, a.ws.xq, a.ws.xd, d.F, brow);
+    st.load(0);
 #pragma unroll 1
     for (int c = 0; c < NC; ++c) {
         __syncthreads();
-        store_chunk(sm, st);
-        const uint2 wsc = wnext;
+        st.store(sm);
         __syncthreads();
-        if (c + 1 < NC) {
-            load_chunk<H>(st, sm, a.ws.xq, a.ws.xd, brow, c + 1);
-            wnext = chunk_scales(srow, c + 1);
-        }
+        if (c + 1 < NC) st.load(c + 1);
 #pragma unroll
-        for (int kb = 0; kb < kKC; ++kb) {
-            const int b = c * kKC + kb;
-            const i32x4 av = *reinterpret_cast<const i32x4 *>(&sm.A[wm * 32 + n][kb * 32 + 16 * half]);
-            const i32x4 gv = *reinterpret_cast<const i32x4 *>(&sm.B[wn * 32 + n][kb * 32 + 16 * half]);
-            const i32x4 uv = *reinterpret_cast<const i32x4 *>(&sm.B[kTN + wn * 32 + n][kb * 32 + 16 * half]);
-            const float dx = sm.sa[kb][wm * 32 + n];
-            const float dw = scale_of(wsc, kb);
-            const v16i zero = {};
-            const v16i cg = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, gv, zero, 0, 0, 0);
-            const v16i cu = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, uv, zero, 0, 0, 0);
+        for (int kb = 0; kb < kKC; kb += 2) {
+            // scale products of blocks kb (registers 0..15) and kb+1 (16..31)
+            const float dx = sm.sa[kb + half][wm * 32 + n];
+            const float dw = wscale(sm, brow_lds, kb + half);
             const v32f pz = {};
             const v32f ps = __builtin_amdgcn_mfma_f32_32x32x1f32(dx, dw, pz, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                accg[i] = __fmaf_rn((float)cg[i], ps[i], accg[i]);
-                accu[i] = __fmaf_rn((float)cu[i], ps[16 + i], accu[i]);
-            }
-            if (DUMP && (col % a.dump.stride == 0)) {
+            for (int j = 0; j < 2; ++j) {
+                const int b = c * kKC + kb + j;
+                const i32x4 av = *reinterpret_cast<const i32x4 *>(&sm.A[wm * 32 + n][(kb + j) * 32 + 16 * half]);
+                const i32x4 bv = *reinterpret_cast<const i32x4 *>(&sm.B[brow_lds][(kb + j) * 32 + 16 * half]);
+                const v16i zero = {};
+                const v16i cv = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int m = wm * 32 + acc_row(i, lane);
-                    if (m < grp.z) {
-                        const int64_t base = ((int64_t)sm.pair[m] * (d.F / a.dump.stride) + col / a.dump.stride) *
-                                                 a.dump.pitch_gu + b;
-                        a.dump.gate_sums[base] = cg[i];
-                        a.dump.up_sums[base] = cu[i];
+                for (int i = 0; i < 16; ++i) acc[i] = __fmaf_rn((float)cv[i], ps[16 * j + i], acc[i]);
+                if (DUMP && (col % a.dump.stride == 0)) {
+                    int32_t *dst = which ? a.dump.up_sums : a.dump.gate_sums;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int m = wm * 32 + acc_row(i, lane);
+                        if (m < grp.z)
+                            dst[((int64_t)sm.pair[m] * (d.F / a.dump.stride) + col / a.dump.stride) * a.dump.pitch_gu +
+                                b] = cv[i];
                     }
                 }
             }
         }
     }
-    // SwiGLU, then quantize each pair's 32 columns (the 32 lanes of this half)
+    // the up waves hand their sums to the gate waves through LDS (the staged
+    // weights are no longer needed): SwiGLU, then quantize each pair's 32
+    // columns (the 32 lanes of a half-wave)
+    __syncthreads();
+    float *hx = reinterpret_cast<float *>(&sm.B[0][0]);  // [64 pairs][64 columns]
+    if (which == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float hv = swiglu(accg[i], accu[i]);
-        const float amax = group_max<32>(fabsf(hv));
-        const float dsc = quant_scale(amax);
-        const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
-        const int m = wm * 32 + acc_row(i, lane);
-        if (m < grp.z) {
-            const int64_t p = sm.pair[m];
-            a.ws.hq[p * d.F + col] = (int8_t)quant_code(hv, inv);
-            if (n == 0) a.ws.hd[p * (d.F / 32) + col / 32] = dsc;
+        for (int i = 0; i < 16; ++i) hx[(wm * 32 + acc_row(i, lane)) * kTN + wn * 32 + n] = acc[i];
+    }
+    __syncthreads();
+    if (which == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = wm * 32 + acc_row(i, lane);
+            const float hv = swiglu(acc[i], hx[m * kTN + wn * 32 + n]);
+            const float amax = group_max<32>(fabsf(hv));
+            const float dsc = quant_scale(amax);
+            const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
+            if (m < grp.z) {
+                const int64_t p = sm.pair[m];
+                a.ws.hq[p * d.F + col] = (int8_t)quant_code(hv, inv);
+                if (n == 0) a.ws.hd[p * (d.F / 32) + col / 32] = dsc;
+            }
         }
     }
 }
@@ -228,46 +252,45 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(LayerArgs a) {
     const int wm = wave >> 1, wn = wave & 1;
     const uint8_t *dmat = shared ? a.wt.sh_down : a.wt.down + grp.x * q8_bytes(d.H, F);
     const int r0 = blockIdx.x * kTN;
-    auto brow = [&](int j) -> const uint8_t * { return dmat + (int64_t)(r0 + j) * F; };
+    auto brow = [&](int j) { return std::make_pair(dmat, r0 + j); };
     const int row = r0 + wn * 32 + n;  // this lane's output row
+    const int brow_lds = wn * 32 + n;
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    // outer product: both halves use this lane's row scale; products j = 0, 1 coincide
-    const uint16_t *srow = reinterpret_cast<const uint16_t *>(dmat + (int64_t)d.H * F) + (int64_t)row * NB;
-    Stage<NBR> st;
-    load_chunk<F>(st, sm, a.ws.hq, a.ws.hd, brow, 0);
-    uint2 wnext = chunk_scales(srow, 0);
+    Stage<256, NBR> st;
+    st.template setup<F>(sm, a.ws.hq, a.ws.hd, d.H, brow);
+    st.load(0);
 #pragma unroll 1
     for (int c = 0; c < NC; ++c) {
         __syncthreads();
-        store_chunk(sm, st);
-        const uint2 wsc = wnext;
+        st.store(sm);
         __syncthreads();
-        if (c + 1 < NC) {
-            load_chunk<F>(st, sm, a.ws.hq, a.ws.hd, brow, c + 1);
-            wnext = chunk_scales(srow, c + 1);
-        }
+        if (c + 1 < NC) st.load(c + 1);
 #pragma unroll
-        for (int kb = 0; kb < kKC; ++kb) {
-            const int b = c * kKC + kb;
-            const i32x4 av = *reinterpret_cast<const i32x4 *>(&sm.A[wm * 32 + n][kb * 32 + 16 * half]);
-            const i32x4 wv = *reinterpret_cast<const i32x4 *>(&sm.B[wn * 32 + n][kb * 32 + 16 * half]);
-            const float dh = sm.sa[kb][wm * 32 + n];
-            const float dw = scale_of(wsc, kb);
-            const v16i zero = {};
-            const v16i cv = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, wv, zero, 0, 0, 0);
+        for (int kb = 0; kb < kKC; kb += 2) {
+            // scale products of blocks kb (registers 0..15) and kb+1 (16..31)
+            const float dh = sm.sa[kb + half][wm * 32 + n];
+            const float dw = wscale(sm, brow_lds, kb + half);
             const v32f pz = {};
             const v32f ps = __builtin_amdgcn_mfma_f32_32x32x1f32(dh, dw, pz, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = __fmaf_rn((float)cv[i], ps[i], acc[i]);
-            if (DUMP && (row % a.dump.stride == 0)) {
+            for (int j = 0; j < 2; ++j) {
+                const int b = c * kKC + kb + j;
+                const i32x4 av = *reinterpret_cast<const i32x4 *>(&sm.A[wm * 32 + n][(kb + j) * 32 + 16 * half]);
+                const i32x4 wv = *reinterpret_cast<const i32x4 *>(&sm.B[wn * 32 + n][(kb + j) * 32 + 16 * half]);
+                const v16i zero = {};
+                const v16i cv = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, wv, zero, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int m = wm * 32 + acc_row(i, lane);
-                    if (m < grp.z)
-                        a.dump.down_sums[((int64_t)sm.pair[m] * (d.H / a.dump.stride) + row / a.dump.stride) *
-                                             a.dump.pitch_dn + b] = cv[i];
+                for (int i = 0; i < 16; ++i) acc[i] = __fmaf_rn((float)cv[i], ps[16 * j + i], acc[i]);
+                if (DUMP && (row % a.dump.stride == 0)) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int m = wm * 32 + acc_row(i, lane);
+                        if (m < grp.z)
+                            a.dump.down_sums[((int64_t)sm.pair[m] * (d.H / a.dump.stride) + row / a.dump.stride) *
+                                                 a.dump.pitch_dn + b] = cv[i];
+                    }
                 }
             }
         }
@@ -283,11 +306,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(LayerArgs a) {
 template <bool DUMP>
 static hipError_t gateup_m(const LayerArgs &a, dim3 grid, hipStream_t s) {
     switch (a.d.H) {
-        case 256: klaunch(gateup_mfma_kernel<256, DUMP>, grid, 256, s, a); break;
-        case 512: klaunch(gateup_mfma_kernel<512, DUMP>, grid, 256, s, a); break;
-        case 1024: klaunch(gateup_mfma_kernel<1024, DUMP>, grid, 256, s, a); break;
-        case 2048: klaunch(gateup_mfma_kernel<2048, DUMP>, grid, 256, s, a); break;
-        case 4096: klaunch(gateup_mfma_kernel<4096, DUMP>, grid, 256, s, a); break;
+        case 256: klaunch(gateup_mfma_kernel<256, DUMP>, grid, 512, s, a); break;
+        case 512: klaunch(gateup_mfma_kernel<512, DUMP>, grid, 512, s, a); break;
+        case 1024: klaunch(gateup_mfma_kernel<1024, DUMP>, grid, 512, s, a); break;
+        case 2048: klaunch(gateup_mfma_kernel<2048, DUMP>, grid, 512, s, a); break;
+        case 4096: klaunch(gateup_mfma_kernel<4096, DUMP>, grid, 512, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
