@@ -146,6 +146,11 @@ SMALL = [
     ms.LayerConfig("q8_noshared_k1", 256, 8, 1, 256, 5, shared=False, seed=19),
     ms.LayerConfig("q8_all_experts", 256, 8, 8, 128, 6, seed=20),
     ms.LayerConfig("q8_nobias_T1", 1024, 64, 6, 512, 1, bias=False, seed=21),
+    ms.LayerConfig("q8_hash_T1", 512, 32, 6, 256, 1, route="hash", vocab=300, seed=34),
+    ms.LayerConfig("q2_learned_T1", 512, 32, 4, 512, 1, routed_fmt="q2", seed=35),
+    ms.LayerConfig("q8_noshared_T1", 256, 16, 3, 128, 1, shared=False, seed=36),
+    ms.LayerConfig("q2_hash_noshared_T1", 1024, 8, 2, 512, 1, routed_fmt="q2", route="hash", vocab=7, shared=False,
+                   seed=37),
     ms.LayerConfig("q2_hash_T32", 512, 16, 6, 512, 32, routed_fmt="q2", route="hash", vocab=64, seed=22),
     ms.LayerConfig("q8_mfma_1024_T300", 1024, 16, 4, 512, 300, seed=26),
     ms.LayerConfig("q8_mfma_hash_T77", 512, 64, 6, 256, 77, route="hash", vocab=5000, seed=27),
@@ -255,6 +260,42 @@ def test_out_of_range_token_id_is_flagged_not_faulted():
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
     assert layer.flags() & 1
+
+
+def test_out_of_range_token_id_is_flagged_one_token():
+    cfg = ms.LayerConfig("bad_token_T1", 256, 16, 2, 128, 1, route="hash", vocab=100, seed=38)
+    inp, layer = case(cfg)
+    x = torch.from_numpy(inp["x"]).cuda()
+    layer.forward(x, torch.tensor([7], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert layer.flags() == 0
+    out = layer.forward(x, torch.tensor([100], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert layer.flags() & 1
+
+
+def test_repeated_expert_in_an_unchecked_hash_row():
+    """A table row naming one expert twice (rejected by the table check, used
+    anyway): one-token calls and a batched call agree bit for bit, and the
+    work list holds the repeated expert once with two pairs."""
+    qr = _qr()
+    cfg = ms.LayerConfig("hash_dup", 512, 16, 4, 256, 6, route="hash", vocab=8, seed=39)
+    inp = ms.make_inputs(cfg)
+    inp["hash_table"][3] = np.array([5, 9, 5, 2], dtype=np.int32)
+    layer = qr.MoELayer(512, 16, 4, 256, True, "q8", "hash", 8).load(inp)
+    x = torch.from_numpy(inp["x"]).cuda()
+    tok = torch.tensor([3, 1, 3, 0, 3, 7], dtype=torch.int32, device="cuda")
+    batched = layer.forward(x, tok).clone()
+    torch.cuda.synchronize()
+    for t in range(cfg.tokens):
+        one = layer.forward(x[t:t + 1].contiguous(), tok[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(one.view(torch.int32), batched[t:t + 1].view(torch.int32)), f"token {t}"
+    r = layer.forward_debug(x[0:1].contiguous(), tok[0:1].contiguous())
+    torch.cuda.synchronize()
+    assert r["counts"].cpu().numpy()[5] == 2 and int((r["counts"] > 0).sum()) == 3
+    assert torch.isfinite(batched).all()
 
 
 def test_check_hash_table():
