@@ -130,6 +130,9 @@ typedef struct moe_debug {
 
 int moe_abi_version(void);
 const char *moe_status_string(int status);
+/* Name of the last HIP error behind an MOE_ERR_HIP returned on the calling
+ * thread ("hipSuccess" if there was none).  The string is static. */
+const char *moe_last_hip_error(void);
 
 /* Bytes of one matrix [rows][cols] in fmt (canonical and packed layouts have
  * the same size), or -1 when cols does not fit the format. */

@@ -10,6 +10,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# One HIP runtime per process: PyTorch ships its own libamdhip64, and once it
+# is loaded the library's dependency of the same name resolves to it.  Loading
+# the library first would map a second runtime next to PyTorch's, and calls
+# through that one find no device.
+import torch  # noqa: F401  (load order, see above)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqrmoe.so")
 
@@ -30,7 +36,10 @@ ALIGN = 256
 class MoEError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {_lib.moe_status_string(status).decode()} (status {status})")
+        msg = f"{what}: {_lib.moe_status_string(status).decode()} (status {status})"
+        if status == -5:  # MOE_ERR_HIP
+            msg += f": {_lib.moe_last_hip_error().decode()}"
+        super().__init__(msg)
 
 
 class Shape(ctypes.Structure):
@@ -53,6 +62,7 @@ _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_
 _SIGS = {
     "moe_abi_version": ([], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_last_hip_error": ([], ctypes.c_char_p),
     "moe_matrix_bytes": ([_I32, _I64, _I64], _I64),
     "moe_pack_weights": ([_I32, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "moe_check_hash_table": ([_P, _I32, _I32, _I32, _P, _SZ, ctypes.POINTER(_I32), _P], ctypes.c_int),

@@ -13,6 +13,15 @@ using namespace qrmoe;
 
 namespace {
 
+// Last HIP failure seen by a library call on this thread (hipSuccess if none).
+thread_local hipError_t t_last_hip = hipSuccess;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MOE_OK;
+    t_last_hip = e;
+    return MOE_ERR_HIP;
+}
+
 constexpr size_t kAlign = 256;
 constexpr int kMfmaTile = 64;  // pairs per MFMA work tile
 
@@ -240,7 +249,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
         cp(dbg->hq, a.ws.hq, P * F);
         cp(dbg->hd, a.ws.hd, P * (F / 32) * 4);
     }
-    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return hip_status(err);
 }
 
 }  // namespace
@@ -263,6 +272,8 @@ const char *moe_status_string(int status) {
     }
 }
 
+const char *moe_last_hip_error(void) { return hipGetErrorName(t_last_hip); }
+
 int64_t moe_matrix_bytes(int32_t fmt, int64_t rows, int64_t cols) {
     if (rows < 0 || cols <= 0) return -1;
     if (fmt == MOE_FMT_Q8_32 && cols % 32 == 0) return q8_bytes(rows, cols);
@@ -280,7 +291,7 @@ int moe_pack_weights(int32_t fmt, const void *canonical, void *packed, int64_t n
     if (n_mats == 0 || rows == 0) return MOE_OK;
     hipError_t err = launch_pack(fmt, (const uint8_t *)canonical, (uint8_t *)packed, n_mats, rows, cols,
                                  (hipStream_t)stream);
-    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return hip_status(err);
 }
 
 int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t top_k, int32_t n_experts, void *workspace,
@@ -294,7 +305,7 @@ int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t top_k, int
     int32_t host = 0;
     if (err == hipSuccess) err = hipMemcpyAsync(&host, res, 4, hipMemcpyDeviceToHost, s);
     if (err == hipSuccess) err = hipStreamSynchronize(s);
-    if (err != hipSuccess) return MOE_ERR_HIP;
+    if (err != hipSuccess) return hip_status(err);
     if (bad_row) *bad_row = host == INT32_MAX ? -1 : host;
     return host == INT32_MAX ? MOE_OK : MOE_ERR_BAD_TABLE;
 }
@@ -308,7 +319,7 @@ int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
     if (!workspace || !aligned(workspace, kAlign)) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < (size_t)kCtlWords * 4) return MOE_ERR_WORKSPACE;
     hipError_t err = launch_ws_init((int32_t *)workspace, kCtlWords, (hipStream_t)stream);
-    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return hip_status(err);
 }
 
 int moe_workspace_flags(void *workspace, int32_t *flags, void *stream) {
@@ -318,7 +329,7 @@ int moe_workspace_flags(void *workspace, int32_t *flags, void *stream) {
     int32_t host = 0;
     hipError_t err = hipMemcpyAsync(&host, dev, 4, hipMemcpyDeviceToHost, s);
     if (err == hipSuccess) err = hipStreamSynchronize(s);
-    if (err != hipSuccess) return MOE_ERR_HIP;
+    if (err != hipSuccess) return hip_status(err);
     *flags = host;
     return MOE_OK;
 }
@@ -345,11 +356,12 @@ int moe_prof_create(moe_prof **prof, int32_t max_events) {
     moe_prof *p = new moe_prof();
     p->pool.resize((size_t)max_events);
     for (auto &e : p->pool) {
-        if (hipEventCreate(&e) != hipSuccess) {
+        const hipError_t ce = hipEventCreate(&e);
+        if (ce != hipSuccess) {
             for (auto &f : p->pool)
                 if (f) hipEventDestroy(f);
             delete p;
-            return MOE_ERR_HIP;
+            return hip_status(ce);
         }
     }
     *prof = p;
@@ -371,9 +383,10 @@ int moe_prof_attach(moe_prof *prof) {
 int moe_prof_collect(moe_prof *prof, float *stage_ms, int32_t *stage_launches, int32_t n_stages) {
     if (!prof || !stage_ms || !stage_launches || n_stages < 1) return MOE_ERR_INVALID_ARG;
     for (auto &ev : prof->used) {
-        if (hipEventSynchronize(ev.b) != hipSuccess) return MOE_ERR_HIP;
+        hipError_t e = hipEventSynchronize(ev.b);
         float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, ev.a, ev.b) != hipSuccess) return MOE_ERR_HIP;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev.a, ev.b);
+        if (e != hipSuccess) return hip_status(e);
         if (ev.stage < n_stages) {
             stage_ms[ev.stage] += ms;
             stage_launches[ev.stage] += 1;

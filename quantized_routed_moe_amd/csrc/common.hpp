@@ -96,18 +96,88 @@ struct LayerArgs {
 // ------------------------------------------------------------------ device
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// ------------------------------------------------ cross-lane butterflies
+// Reductions over aligned groups of W lanes (W a power of two up to 64) as an
+// xor butterfly, smallest distance first, every lane of a group ending with
+// the same value.  Partner values come from registers, not from LDS:
+//  - xor 1, xor 2: DPP quad permutations [1,0,3,2] and [2,3,0,1];
+//  - xor 4, xor 8: DPP half-row mirror (l <-> 7-l) and row mirror
+//    (l <-> 15-l).  After the previous steps every lane of a 4-lane (8-lane)
+//    group holds the same value, so the mirror partner's value equals the
+//    xor-4 (xor-8) partner's;
+//  - xor 16, xor 32: v_permlane16_swap / v_permlane32_swap, which exchange
+//    the odd 16-lane rows (upper 32 lanes) of one copy with the even rows
+//    (lower 32 lanes) of another, so lane l sees lane l^16 (l^32).
+// Each step combines the two values commutatively, so partners compute the
+// same bits.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+// The two 32-bit values of the butterfly pair at distance D, as (this lane's,
+// partner's) for D <= 8 and as (lower lane's, upper lane's) for D = 16, 32.
+template <int D>
+__device__ __forceinline__ void bfly_pair_u32(uint32_t v, uint32_t &a, uint32_t &b) {
+    if constexpr (D <= 8) {
+        constexpr int ctrl = D == 1 ? 0xB1 : D == 2 ? 0x4E : D == 4 ? 0x141 : 0x140;
+        a = v;
+        b = dpp_u32<ctrl>(v);
+    } else if constexpr (D == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        a = p[0];
+        b = p[1];
+    } else {
+        static_assert(D == 32, "butterfly distance");
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        a = p[0];
+        b = p[1];
+    }
+}
+
+template <int D, class Op>
+__device__ __forceinline__ float bfly_step(float v, Op op) {
+    uint32_t a, b;
+    bfly_pair_u32<D>(__float_as_uint(v), a, b);
+    return op(__uint_as_float(a), __uint_as_float(b));
+}
+
+template <int D, class Op>
+__device__ __forceinline__ double bfly_step(double v, Op op) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    uint32_t la, lb, ha, hb;
+    bfly_pair_u32<D>((uint32_t)u, la, lb);
+    bfly_pair_u32<D>((uint32_t)(u >> 32), ha, hb);
+    return op(__longlong_as_double((long long)(((uint64_t)ha << 32) | la)),
+              __longlong_as_double((long long)(((uint64_t)hb << 32) | lb)));
+}
+
+template <int W, class T, class Op>
+__device__ __forceinline__ T group_reduce(T v, Op op) {
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+    if constexpr (W >= 2) v = bfly_step<1>(v, op);
+    if constexpr (W >= 4) v = bfly_step<2>(v, op);
+    if constexpr (W >= 8) v = bfly_step<4>(v, op);
+    if constexpr (W >= 16) v = bfly_step<8>(v, op);
+    if constexpr (W >= 32) v = bfly_step<16>(v, op);
+    if constexpr (W >= 64) v = bfly_step<32>(v, op);
     return v;
 }
 
 template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    return group_reduce<W>(v, [](float a, float b) { return a + b; });
+}
+
+// fp64 sum over the whole wave: the adjacent-pair tree of the 64 lane values
+// (lane l's value is leaf l).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    return group_reduce<64>(v, [](double a, double b) { return a + b; });
+}
+
+template <int W>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return group_reduce<W>(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }

@@ -46,9 +46,8 @@ __global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_le
             for (int le = blockIdx.x; le < nlog; le += n_lead) {
                 const int t = le / d.E, e = le % d.E;
                 const int off = wave * (H / 4) + lane * SEG;
-                double v = segment_tree<SEG>(a.x + (int64_t)t * H + off, a.wt.router_w + (int64_t)e * H + off);
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+                const double v = wave_sum_f64(
+                    segment_tree<SEG>(a.x + (int64_t)t * H + off, a.wt.router_w + (int64_t)e * H + off));
                 if (lane == 0) sm.part[wave] = v;
                 __syncthreads();
                 if (tid == 0) {

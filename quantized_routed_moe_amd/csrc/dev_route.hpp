@@ -67,10 +67,7 @@ __device__ __forceinline__ double segment_tree(const float *__restrict__ xa, con
 template <int H>
 __device__ __forceinline__ float wave_logit(const float *__restrict__ xrow, const float *__restrict__ wrow, int lane) {
     constexpr int SEG = H / 64;
-    double v = segment_tree<SEG>(xrow + lane * SEG, wrow + lane * SEG);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    return (float)v;
+    return (float)wave_sum_f64(segment_tree<SEG>(xrow + lane * SEG, wrow + lane * SEG));
 }
 
 // ------------------------------------------------------------- selection

@@ -121,3 +121,15 @@ def test_profiler_argument_checks():
     assert L.moe_prof_create(ctypes.byref(h), 1) == INVALID
     assert L.moe_prof_create(None, 16) == INVALID
     assert L.moe_stage_name(5) == b"gateup" and L.moe_stage_name(99) == b"?"
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding before torch must not map a second HIP runtime
+    (the library has to use the runtime that owns torch's device memory)."""
+    import subprocess
+    import sys
+    code = ("import quantized_routed_moe_amd, torch\n"
+            "print('\\n'.join(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l})))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__)))).stdout.split()
+    assert len(out) == 1, out
