@@ -209,6 +209,7 @@ struct Sel1Smem {
 };
 
 constexpr int kG1Rows = 64;   // rows of one workgroup: two h blocks
+constexpr int kMaxSelList = 9;  // work-list entries the one-token down kernel reads (top_k <= 8, shared)
 constexpr int kG1Waves = 8;
 
 template <int K, int FMT, bool DUMP>
@@ -301,6 +302,8 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
         if (tid < nuniq) {
             const int f = ss.first[tid], n = (tid + 1 < nuniq ? ss.first[tid + 1] : k) - f;
             a.ws.groups[tid] = make_int4(ss.uniq[tid], f, n, ss.pairs[f]);
+        } else if (tid >= nuniq + d.has_shared && tid < kMaxSelList) {
+            a.ws.groups[tid] = make_int4(0, 0, 0, 0);  // entries past the list name group 0's pair
         }
         if (tid == 0) {
             a.ws.offsets[d.E] = k;
@@ -331,9 +334,11 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
 // Rows of the output: each wave pass covers RPW rows (LPR lanes per row, the
 // routed format's geometry; the shared Q8 expert reuses it with more chunks
 // per lane).  Every selected expert's row is requested before h is staged.
-constexpr int kMaxSel = 9;  // top_k <= 8 plus the shared expert
+constexpr int kMaxSel = kMaxSelList;  // top_k <= 8 plus the shared expert
 
-template <int F, int FMT, bool DUMP>
+// NR routed row slots per lane (top_k <= NR); every slot is loaded and
+// reduced, the ones past the routed groups are dropped at the combine.
+template <int F, int FMT, bool DUMP, int NR>
 __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
     constexpr int L = DefLpr<F, FMT>::v;
     constexpr int RPW = 64 / L;
@@ -360,21 +365,20 @@ __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
     const int G = a.ws.ctl[kCtlGroups];
     const int nr = d.has_shared ? G - 1 : G;
     // pair of group `i` by a chain of selects (constant register indices)
-    int pown = gp[0];
-#pragma unroll
-    for (int j = 1; j < kMaxSel; ++j) pown = tid == j ? gp[j] : pown;
-    float wown = 1.0f;
-    if (tid < nr) wown = a.ws.w[pown];
+#define QRMOE_PAIR_OF(out, i)                                      \
+    int out = gp[0];                                               \
+    _Pragma("unroll") for (int j_ = 1; j_ < kMaxSel; ++j_) out = (i) == j_ ? gp[j_] : out
+    QRMOE_PAIR_OF(pown, tid);
+    // work-list entries past the G groups were never written: their pairs
+    // index nothing, so threads past the routed groups read group 0's weight
+    const float wraw = a.ws.w[tid < nr ? pown : gp[0]];
     // h block scales: loads now, LDS after the rows are requested
     float hdv[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
         const int idx = tid + 256 * u;
         const bool ok = idx < G * (F / 32);
-        const int tok = ok ? idx / (F / 32) : 0;
-        int p = gp[0];
-#pragma unroll
-        for (int j = 1; j < kMaxSel; ++j) p = tok == j ? gp[j] : p;
+        QRMOE_PAIR_OF(p, ok ? idx / (F / 32) : 0);
         hdv[u] = a.ws.hd[(int64_t)p * (F / 32) + (ok ? idx % (F / 32) : 0)];
     }
     // h codes of the G pairs go straight to LDS (aq rows are contiguous): one
@@ -384,23 +388,21 @@ __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
         const int ninst = G * F / 1024;
         for (int j = wave; j < ninst; j += 4) {
             const int o = j * 1024 + lane * 16;
-            const int tok = o / F;
-            int p = gp[0];
-#pragma unroll
-            for (int jj = 1; jj < kMaxSel; ++jj) p = tok == jj ? gp[jj] : p;
+            QRMOE_PAIR_OF(p, o / F);
             __builtin_amdgcn_global_load_lds(a.ws.hq + (int64_t)p * F + o % F,
                                              (lds_ptr)(&sm.aq[0][0] + j * 1024), 16, 0, 0);
         }
     }
+#undef QRMOE_PAIR_OF
     // Every slot loads without a branch (a slot past the routed groups re-reads
     // group 0's row, served by the cache), so nothing is sunk below the rows.
     const int64_t mb = mat_bytes(FMT, d.H, F);
-    RowRegs<F, FMT, L> rr[kMaxSel - 1];
+    RowRegs<F, FMT, L> rr[NR];
 #pragma unroll
-    for (int i = 0; i < kMaxSel - 1; ++i) rr[i].load(a.wt.down + (int64_t)(i < nr ? gx[i] : gx[0]) * mb, d.H, r, seg);
+    for (int i = 0; i < NR; ++i) rr[i].load(a.wt.down + (int64_t)(i < nr ? gx[i] : gx[0]) * mb, d.H, r, seg);
     if (tid < G) {
         sm.pair[tid] = pown;
-        sm.w[tid] = wown;
+        sm.w[tid] = tid < nr ? wraw : 1.0f;
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -425,26 +427,30 @@ __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
     }
     // Same arithmetic per expert as the batched down + combine: y = w * (sum
     // over lanes), summed in ascending expert id, the shared expert last.
+    // The shared expert's row was requested first, so it is reduced first.
     const bool dump_row = DUMP && (r % a.dump.stride == 0);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxSel - 1; ++i)
-        if (i < nr) {
-            int32_t *dd = dump_row ? a.dump.down_sums +
-                                         ((int64_t)sm.pair[i] * (d.H / a.dump.stride) + r / a.dump.stride) *
-                                             a.dump.pitch_dn
-                                   : nullptr;
-            const float y = group_sum<L>(lane_dot<F, L>(rr[i], sm.aq[i], sm.ad[i], sm.as16[i], seg, dd));
-            acc = __fadd_rn(acc, __fmul_rn(sm.w[i], y));
-        }
+    float ysh = 0.0f;
     if (d.has_shared) {
         int32_t *dd = dump_row ? a.dump.down_sums +
                                      ((int64_t)sm.pair[nr] * (d.H / a.dump.stride) + r / a.dump.stride) *
                                          a.dump.pitch_dn
                                : nullptr;
-        const float y = group_sum<L>(lane_dot<F, L>(rsh, sm.aq[nr], sm.ad[nr], sm.as16[nr], seg, dd));
-        acc = __fadd_rn(acc, __fmul_rn(1.0f, y));
+        ysh = group_sum<L>(lane_dot<F, L>(rsh, sm.aq[nr], sm.ad[nr], sm.as16[nr], seg, dd));
     }
+    // The routed slots are reduced without branches; slots past the routed
+    // groups read LDS rows nobody wrote and are dropped here.
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        int32_t *dd = dump_row && i < nr ? a.dump.down_sums +
+                                               ((int64_t)sm.pair[i] * (d.H / a.dump.stride) + r / a.dump.stride) *
+                                                   a.dump.pitch_dn
+                                         : nullptr;
+        const float y = group_sum<L>(lane_dot<F, L>(rr[i], sm.aq[i], sm.ad[i], sm.as16[i], seg, dd));
+        const float t = __fadd_rn(acc, __fmul_rn(sm.w[i], y));
+        acc = i < nr ? t : acc;
+    }
+    if (d.has_shared) acc = __fadd_rn(acc, __fmul_rn(1.0f, ysh));
     if (seg == 0) a.out[r] = acc;
 }
 
@@ -506,7 +512,10 @@ hipError_t launch_decode_gateup1(const LayerArgs &a, bool dump, hipStream_t s) {
 template <int F, int FMT, bool DUMP>
 static hipError_t down1_h(const LayerArgs &a, hipStream_t s) {
     constexpr int RPW = 64 / DefLpr<F, FMT>::v;
-    klaunch(decode_down1_kernel<F, FMT, DUMP>, dim3(a.d.H / (4 * RPW)), dim3(256), s, a);
+    const dim3 grid(a.d.H / (4 * RPW)), block(256);
+    if (a.d.k <= 2) klaunch(decode_down1_kernel<F, FMT, DUMP, 2>, grid, block, s, a);
+    else if (a.d.k <= 6) klaunch(decode_down1_kernel<F, FMT, DUMP, 6>, grid, block, s, a);
+    else klaunch(decode_down1_kernel<F, FMT, DUMP, kMaxSel - 1>, grid, block, s, a);
     return hipGetLastError();
 }
 
