@@ -114,106 +114,154 @@ hipError_t launch_quant(const LayerArgs &a, hipStream_t s) {
 }
 
 // Tiled logits: a workgroup computes a 32-token x 32-expert tile, each thread
-// 2 tokens x 2 experts.  The H-long sum is the adjacent-pair tree: chunks of
-// 64 elements staged in LDS give the level-6 nodes, and the chunk loop is a
-// compile-time recursion that combines chunk sums in the same tree order.
+// 2 tokens x 2 experts.  The H-long sum is the adjacent-pair tree of the
+// exact fp64 products:
+//  - chunks of 64 elements of the tile's x and W rows are staged in LDS as
+//    fp32 (fp64 rows would double the LDS traffic per product, which then
+//    bounds the kernel); the next chunk's global loads are in flight while
+//    the current one is reduced;
+//  - each 8-element run gives a level-3 node in registers, its level-1 nodes
+//    as fma(x1, w1, x0 * w0) (both products are exact in fp64, so this
+//    rounds exactly like the sum of the two products); the chunk's 8 runs
+//    combine into its level-6 node by a compile-time tree;
+//  - the chunk nodes are merged by a binary counter: after chunk c, merge
+//    with the stacked left siblings once per trailing one bit of c.  With
+//    2^m chunks this is exactly the adjacent-pair tree; the merges are
+//    uniform branches, no dynamic indexing.
 constexpr int kLogTile = 32;
 constexpr int kLogChunk = 64;
+constexpr int kLogRun = 8;      // elements per register subtree (a level-3 node)
+constexpr int kLogLevels = 7;   // stack levels: up to 2^6 chunks, H <= 4096
+constexpr int kLogPad = 4;      // row padding (keeps 16-byte rows aligned)
 
 struct LogitsSmem {
-    float xs[kLogTile][kLogChunk + 4];
-    float wsm[kLogTile][kLogChunk + 4];
+    alignas(16) float xs[kLogTile][kLogChunk + kLogPad];
+    alignas(16) float wsm[kLogTile][kLogChunk + kLogPad];
 };
 
+// One thread's share of a chunk in registers: 2 float4 of x rows, 2 of W rows.
+struct LogitChunkRegs {
+    float4 x[2], w[2];
+    __device__ __forceinline__ void load(const float *__restrict__ x0, const float *__restrict__ w0, int H, int T,
+                                         int E, int tb, int eb, int c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = threadIdx.x + 256 * i, row = idx >> 4, col = (idx & 15) * 4;
+            const int t = tb + row, e = eb + row;
+            // rows past T / E read row 0 of the tile and are zeroed at the store
+            x[i] = *reinterpret_cast<const float4 *>(x0 + (int64_t)(t < T ? t : tb) * H + c * kLogChunk + col);
+            w[i] = *reinterpret_cast<const float4 *>(w0 + (int64_t)(e < E ? e : eb) * H + c * kLogChunk + col);
+        }
+    }
+    // (component selects: a select of whole float4 values goes through memory)
+    static __device__ __forceinline__ float4 keep(bool ok, float4 v) {
+        return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
+    }
+    __device__ __forceinline__ void store(LogitsSmem &sm, int T, int E, int tb, int eb) const {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = threadIdx.x + 256 * i, row = idx >> 4, col = (idx & 15) * 4;
+            *reinterpret_cast<float4 *>(&sm.xs[row][col]) = keep(tb + row < T, x[i]);
+            *reinterpret_cast<float4 *>(&sm.wsm[row][col]) = keep(eb + row < E, w[i]);
+        }
+    }
+};
+
+// Level-3 nodes of the 4 (token, expert) pairs of this thread over the run
+// of 8 elements at i0 of the staged chunk (each element converted to fp64
+// where it is used).
+__device__ __forceinline__ void logit_run(const LogitsSmem &sm, int t0, int e0, int i0, double r[4]) {
+    float xa[2][kLogRun], wa[2][kLogRun];
+#pragma unroll
+    for (int q = 0; q < kLogRun; q += 4) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float4 xv = *reinterpret_cast<const float4 *>(&sm.xs[t0 + 16 * k][i0 + q]);
+            const float4 wv = *reinterpret_cast<const float4 *>(&sm.wsm[e0 + 16 * k][i0 + q]);
+            xa[k][q] = xv.x;
+            xa[k][q + 1] = xv.y;
+            xa[k][q + 2] = xv.z;
+            xa[k][q + 3] = xv.w;
+            wa[k][q] = wv.x;
+            wa[k][q + 1] = wv.y;
+            wa[k][q + 2] = wv.z;
+            wa[k][q + 3] = wv.w;
+        }
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int ei = 0; ei < 2; ++ei) {
+            double n1[kLogRun / 2];
+#pragma unroll
+            for (int j = 0; j < kLogRun / 2; ++j)
+                n1[j] = __fma_rn((double)xa[ti][2 * j + 1], (double)wa[ei][2 * j + 1],
+                                 __dmul_rn((double)xa[ti][2 * j], (double)wa[ei][2 * j]));
+            r[ti * 2 + ei] = __dadd_rn(__dadd_rn(n1[0], n1[1]), __dadd_rn(n1[2], n1[3]));
+        }
+}
+
+// Node over the N elements at i0 (N a multiple of the run) of the staged chunk.
 template <int N>
-__device__ __forceinline__ void tile_prod_tree(const LogitsSmem &sm, int t0, int e0, int i0, double r[4]) {
-    if constexpr (N == 4) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(&sm.xs[t0][i0]);
-        const float4 x1 = *reinterpret_cast<const float4 *>(&sm.xs[t0 + 16][i0]);
-        const float4 w0 = *reinterpret_cast<const float4 *>(&sm.wsm[e0][i0]);
-        const float4 w1 = *reinterpret_cast<const float4 *>(&sm.wsm[e0 + 16][i0]);
-        const float xa[2][4] = {{x0.x, x0.y, x0.z, x0.w}, {x1.x, x1.y, x1.z, x1.w}};
-        const float wa[2][4] = {{w0.x, w0.y, w0.z, w0.w}, {w1.x, w1.y, w1.z, w1.w}};
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-            for (int ei = 0; ei < 2; ++ei) r[ti * 2 + ei] = prod_tree<4>(xa[ti], wa[ei]);
+__device__ __forceinline__ void logit_tree(const LogitsSmem &sm, int t0, int e0, int i0, double r[4]) {
+    if constexpr (N == kLogRun) {
+        logit_run(sm, t0, e0, i0, r);
     } else {
         double a[4], b[4];
-        tile_prod_tree<N / 2>(sm, t0, e0, i0, a);
-        tile_prod_tree<N / 2>(sm, t0, e0, i0 + N / 2, b);
+        logit_tree<N / 2>(sm, t0, e0, i0, a);
+        logit_tree<N / 2>(sm, t0, e0, i0 + N / 2, b);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = a[i] + b[i];
+        for (int i = 0; i < 4; ++i) r[i] = __dadd_rn(a[i], b[i]);
     }
 }
 
-// Stage chunk c0 (64 elements) of the tile's 32 x-rows and 32 W-rows into LDS.
-__device__ __forceinline__ void stage_logit_chunk(LogitsSmem &sm, const float *__restrict__ x,
-                                                  const float *__restrict__ w, int H, int T, int E, int tb, int eb,
-                                                  int c0) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 4, col = (idx & 15) * 4;
-        const int t = tb + row, e = eb + row;
-        float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), wv = xv;
-        if (t < T) xv = *reinterpret_cast<const float4 *>(x + (int64_t)t * H + c0 * kLogChunk + col);
-        if (e < E) wv = *reinterpret_cast<const float4 *>(w + (int64_t)e * H + c0 * kLogChunk + col);
-        *reinterpret_cast<float4 *>(&sm.xs[row][col]) = xv;
-        *reinterpret_cast<float4 *>(&sm.wsm[row][col]) = wv;
-    }
-}
-
-// The chunk sums (level-6 nodes of the tree) are merged with a binary
-// counter: after chunk c, merge with the stacked left siblings once per
-// trailing one bit of c.  With 2^m chunks this yields exactly the
-// adjacent-pair tree; the merges are uniform branches, no dynamic indexing.
 __global__ __launch_bounds__(256) void logits_tiled_kernel(LayerArgs a) {
     __shared__ LogitsSmem sm;
-    const int H = a.d.H;
+    const int H = a.d.H, T = a.d.T, E = a.d.E;
     const int tb = blockIdx.x * kLogTile, eb = blockIdx.y * kLogTile;
+    const int t0 = threadIdx.x >> 4, e0 = threadIdx.x & 15;
     const int nch = H / kLogChunk;
-    double st[7][4];
+    double st[kLogLevels][4];
 #pragma unroll
-    for (int l = 0; l < 7; ++l)
+    for (int l = 0; l < kLogLevels; ++l)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[l][i] = 0.0;
+    LogitChunkRegs cr;
+    cr.load(a.x, a.wt.router_w, H, T, E, tb, eb, 0);
     for (int c = 0; c < nch; ++c) {
+        __syncthreads();  // the previous chunk's reads are done
+        cr.store(sm, T, E, tb, eb);
         __syncthreads();
-        stage_logit_chunk(sm, a.x, a.wt.router_w, H, a.d.T, a.d.E, tb, eb, c);
-        __syncthreads();
+        if (c + 1 < nch) cr.load(a.x, a.wt.router_w, H, T, E, tb, eb, c + 1);
         double v[4];
-        tile_prod_tree<kLogChunk>(sm, threadIdx.x >> 4, threadIdx.x & 15, 0, v);
+        logit_tree<kLogChunk>(sm, t0, e0, 0, v);
         const int ones = __builtin_ctz(~c);
 #pragma unroll
-        for (int l = 0; l < 6; ++l)
+        for (int l = 0; l < kLogLevels - 1; ++l)
             if (l < ones)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = st[l][i] + v[i];
+                for (int i = 0; i < 4; ++i) v[i] = __dadd_rn(st[l][i], v[i]);
 #pragma unroll
-        for (int l = 0; l < 7; ++l)
+        for (int l = 0; l < kLogLevels; ++l)
             if (l == ones)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) st[l][i] = v[i];
     }
     int top = 0;
-    while ((1 << top) < nch) ++top;  // nch = 2^top, the total sits at level top
-    double r[4];
+    while ((kLogChunk << top) < H) ++top;  // H / 64 = 2^top chunks: the total sits at level top
+    double r[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = 0.0;
-#pragma unroll
-    for (int l = 0; l < 7; ++l)
+    for (int l = 0; l < kLogLevels; ++l)
         if (l == top)
 #pragma unroll
             for (int i = 0; i < 4; ++i) r[i] = st[l][i];
-    const int tl = threadIdx.x >> 4, el = threadIdx.x & 15;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
         for (int ei = 0; ei < 2; ++ei) {
-            const int t = tb + tl + 16 * ti, e = eb + el + 16 * ei;
-            if (t < a.d.T && e < a.d.E) {
-                const int64_t i = (int64_t)t * a.d.E + e;
+            const int t = tb + t0 + 16 * ti, e = eb + e0 + 16 * ei;
+            if (t < T && e < E) {
+                const int64_t i = (int64_t)t * E + e;
                 const float l = (float)r[ti * 2 + ei];
                 a.ws.logits[i] = l;
                 score_key(l, a.wt.router_b, e, a.ws.scores + i, a.ws.keys + i);
@@ -222,7 +270,8 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(LayerArgs a) {
 }
 
 hipError_t launch_logits(const LayerArgs &a, hipStream_t s) {
-    if (a.d.H < kLogChunk || a.d.H > kLogChunk * 64) return hipErrorInvalidValue;
+    // H a power of two (validated with the shape): 2^k whole chunks
+    if (a.d.H < kLogChunk || a.d.H > (kLogChunk << (kLogLevels - 1))) return hipErrorInvalidValue;
     dim3 grid((a.d.T + kLogTile - 1) / kLogTile, (a.d.E + kLogTile - 1) / kLogTile);
     klaunch(logits_tiled_kernel, grid, dim3(256), s, a);
     return hipGetLastError();
