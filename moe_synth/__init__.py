@@ -147,13 +147,21 @@ class LayerConfig:
 
 
 # The five workloads of the layer: a tiny parity case, Q8 decode, decode with
-# 2-bit routed experts, hash-routed batched decode, and a prefill chunk.
+# 2-bit routed experts, hash-routed batched decode, and a prefill chunk; then
+# the same prefill at larger chunks.
 CONFIGS = {
     "tiny": LayerConfig("tiny", 256, 16, 2, 128, 4, seed=0),
     "decode_q8": LayerConfig("decode_q8", 4096, 256, 6, 2048, 1, seed=1),
     "decode_q2": LayerConfig("decode_q2", 4096, 256, 6, 2048, 1, routed_fmt="q2", seed=2),
     "hash_decode": LayerConfig("hash_decode", 4096, 256, 6, 2048, 32, route="hash", seed=3),
     "prefill": LayerConfig("prefill", 4096, 256, 6, 2048, 2048, seed=4),
+    # Larger prefill chunks over the same layer (same seed: identical weights,
+    # x rows prefix-stable): 4096 tokens, the default prefill chunk of page
+    # "DwarfStar (ds4) — ROCm / gfx1151 fork", section "Benchmarking"; 8192,
+    # the chunk of the qualified launch on page "DeepSeek V4 Flash — DFlash
+    # Integration", section "DSpark".
+    "prefill_4096": LayerConfig("prefill_4096", 4096, 256, 6, 2048, 4096, seed=4),
+    "prefill_8192": LayerConfig("prefill_8192", 4096, 256, 6, 2048, 8192, seed=4),
 }
 
 

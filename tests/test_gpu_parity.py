@@ -323,12 +323,18 @@ def test_full_size_decode(name):
 
 
 @pytest.mark.slow
-def test_full_size_prefill_sampled():
+@pytest.mark.parametrize("T", [2048, 4096, 8192])
+def test_full_size_prefill_sampled(T):
+    """Prefill chunks of 2048, 4096 and 8192 tokens over the same layer (the
+    larger ones take further rows of the same x stream): routing, x
+    quantization and the sort of every token bit-exact, outputs and block sums
+    of sampled tokens."""
     cfg = ms.CONFIGS["prefill"]
     inp, layer = case(cfg)
-    g = run_gpu(cfg, inp, layer, stride=128)
-    rows = np.r_[0, 1, 2, 511, 1024, 1500, 2046, 2047, np.arange(37, 2048, 173)]
-    check(cfg, inp, g, rows=np.unique(rows), stride=128)
+    x = inp["x"] if T == cfg.tokens else ms.extra_tokens(cfg, T)
+    g = run_gpu(cfg, inp, layer, x=x, stride=128)
+    rows = np.r_[0, 1, 2, T // 4, T // 2, T - 2, T - 1, np.arange(37, T, T // 12)]
+    check(cfg, inp, g, x=x, rows=np.unique(rows), stride=128, name=f"prefill_T{T}")
     assert np.count_nonzero(g["counts"]) > 0
 
 
