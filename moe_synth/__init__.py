@@ -124,8 +124,11 @@ class LayerConfig:
     hidden/n_experts/top_k/ffn follow the layer shape; ``tokens`` is the batch
     of one call.  ``routed_fmt`` is "q8" (Q8_32) or "q2" (Q2_256) for the routed
     experts; the shared expert is always Q8_32 with the same FFN width.
-    ``route`` is "learned" (sigmoid router, bias-adjusted top-k) or "hash"
-    (token id -> fixed table of k distinct experts, equal weights).
+    ``route`` is "learned" (sigmoid router, bias-adjusted top-k), "hash"
+    (token id -> fixed table of distinct experts, equal weights) or
+    "hash_scored" (the table's experts weighted by their renormalised router
+    scores).  Hash tables have ``table_k`` entries per row (0: top_k), of which
+    the first top_k are used.
     """
     name: str
     hidden: int
@@ -141,6 +144,7 @@ class LayerConfig:
     bias: bool = True
     router_std: float = 0.05
     bias_std: float = 0.1
+    table_k: int = 0
 
     def with_(self, **kw) -> "LayerConfig":
         return replace(self, **kw)
@@ -170,7 +174,7 @@ def make_inputs(cfg: LayerConfig, tokens: int | None = None) -> dict:
 
     x ~ N(0,1) fp32 [T][H]; router W ~ N(0, router_std) fp32 [E][H]; bias ~
     N(0, bias_std) fp32 [E] (zeros when cfg.bias is False); token ids uniform in
-    [0, vocab); hash table [vocab][k] of distinct experts; Q8 codes uniform in
+    [0, vocab); hash table [vocab][table_k or k] of distinct experts; Q8 codes uniform in
     [-127,127] with fp16 scales U(0.001, 0.01); Q2 codes, scales and mins
     uniform over their bit widths with fp16 d, dmin U(0.001, 0.01).
     Rows of x and token ids are prefix-stable in ``tokens``.
@@ -178,13 +182,14 @@ def make_inputs(cfg: LayerConfig, tokens: int | None = None) -> dict:
     T = cfg.tokens if tokens is None else tokens
     H, E, k, F, s = cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.seed
     d = {"x": normal_f32((T, H), 0.0, 1.0, s, TAG["x"])}
-    if cfg.route == "learned":
+    if cfg.route != "hash":
         d["router_w"] = normal_f32((E, H), 0.0, cfg.router_std, s, TAG["router_w"])
+    if cfg.route == "learned":
         d["router_b"] = (normal_f32((E,), 0.0, cfg.bias_std, s, TAG["router_b"]) if cfg.bias
                          else np.zeros(E, dtype=np.float32))
     else:
         d["token_ids"] = uniform_i32(T, 0, cfg.vocab - 1, s, TAG["token_ids"])
-        d["hash_table"] = distinct_rows(cfg.vocab, k, E, s, TAG["hash_table"])
+        d["hash_table"] = distinct_rows(cfg.vocab, cfg.table_k or k, E, s, TAG["hash_table"])
     bank = q8_bank if cfg.routed_fmt == "q8" else q2_bank
     d["gate"] = bank(E, F, H, s, TAG["gate"])
     d["up"] = bank(E, F, H, s, TAG["up"])

@@ -20,7 +20,7 @@ _HDR = os.path.join(_HERE, "moe_oracle.h")
 _LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
 
 FMT = {"q8": 1, "q2": 2}
-ROUTE = {"learned": 1, "hash": 2}
+ROUTE = {"learned": 1, "hash": 2, "hash_scored": 3}
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared"]
 
@@ -36,7 +36,7 @@ def build(force: bool = False) -> str:
 
 class _Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("hidden", "n_experts", "top_k", "ffn", "has_shared", "routed_fmt", "route")]
+                ("hidden", "n_experts", "top_k", "ffn", "has_shared", "routed_fmt", "route", "table_k")]
 
 
 class _Weights(ctypes.Structure):
@@ -62,7 +62,8 @@ def _load():
             "orc_pairwise_sum": ([P, I32], ctypes.c_double),
             "orc_sigmoid": ([F], F),
             "orc_route_learned": ([P, P, I32, I32, I32, P, P, P], None),
-            "orc_route_hash": ([P, P, I32, I32, I32, I32, P, P], ctypes.c_int),
+            "orc_route_hash": ([P, P, I32, I32, I32, I32, I32, P, P], ctypes.c_int),
+            "orc_route_hash_scored": ([P, P, I32, I32, P, I32, I32, I32, P, P], ctypes.c_int),
             "orc_quantize": ([P, I64, P, P], None),
             "orc_sort_pairs": ([P, I32, I32, I32, P, P, P], None),
             "orc_matvec": ([P, I32, I32, I32, P, P, P], None),
@@ -119,12 +120,28 @@ def route_learned(logits: np.ndarray, bias: np.ndarray | None, k: int):
     return ids, w, s
 
 
-def route_hash(token_ids: np.ndarray, table: np.ndarray, n_experts: int):
+def route_hash(token_ids: np.ndarray, table: np.ndarray, n_experts: int, k: int | None = None):
+    """ids/weights from the first k (default: all) entries of each token's table row."""
     T = token_ids.shape[0]
-    vocab, k = table.shape
+    vocab, table_k = table.shape
+    k = table_k if k is None else k
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float32)
-    rc = _load().orc_route_hash(_p(token_ids), _p(table), vocab, T, n_experts, k, _p(ids), _p(w))
+    rc = _load().orc_route_hash(_p(token_ids), _p(table), vocab, table_k, T, n_experts, k, _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError("hash routing: token id or table entry out of range, or duplicate expert in a row")
+    return ids, w
+
+
+def route_hash_scored(token_ids: np.ndarray, table: np.ndarray, logits: np.ndarray, k: int | None = None):
+    """Table-chosen experts weighted by their renormalised router scores."""
+    T, E = logits.shape
+    vocab, table_k = table.shape
+    k = table_k if k is None else k
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    rc = _load().orc_route_hash_scored(_p(token_ids), _p(table), vocab, table_k, _p(logits), T, E, k, _p(ids),
+                                       _p(w))
     if rc != 0:
         raise ValueError("hash routing: token id or table entry out of range, or duplicate expert in a row")
     return ids, w
@@ -180,12 +197,13 @@ def forward(cfg, inp: dict, x: np.ndarray | None = None, token_ids: np.ndarray |
     is the shared expert).
     """
     x = inp["x"] if x is None else np.ascontiguousarray(x, dtype=np.float32)
-    if cfg.route == "hash":
+    if cfg.route != "learned":
         token_ids = inp["token_ids"] if token_ids is None else np.ascontiguousarray(token_ids, dtype=np.int32)
     T, H = x.shape
     E, k, F = cfg.n_experts, cfg.top_k, cfg.ffn
     S = k + 1
-    shape = _Shape(H, E, k, F, 1 if cfg.shared else 0, FMT[cfg.routed_fmt], ROUTE[cfg.route])
+    table_k = inp["hash_table"].shape[1] if cfg.route != "learned" else 0
+    shape = _Shape(H, E, k, F, 1 if cfg.shared else 0, FMT[cfg.routed_fmt], ROUTE[cfg.route], table_k)
     wt = _Weights(_p(inp.get("router_w")), _p(inp.get("router_b")), _p(inp.get("hash_table")),
                   cfg.vocab, _p(inp["gate"]), _p(inp["up"]), _p(inp["down"]),
                   _p(inp.get("sh_gate")), _p(inp.get("sh_up")), _p(inp.get("sh_down")))
@@ -198,7 +216,7 @@ def forward(cfg, inp: dict, x: np.ndarray | None = None, token_ids: np.ndarray |
     g = r.get
     rc = _load().orc_forward(ctypes.byref(shape), ctypes.byref(wt), _p(x), _p(token_ids), T, 1 if dense else 0,
                              _p(r["out"]), _p(g("ids")), _p(g("w")),
-                             _p(g("logits")) if cfg.route == "learned" else None,
+                             _p(g("logits")) if cfg.route != "hash" else None,
                              _p(g("xq")), _p(g("xd")), _p(g("h")), _p(g("hq")), _p(g("hd")))
     if rc != 0:
         raise ValueError("oracle forward rejected its input")

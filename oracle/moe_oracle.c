@@ -29,7 +29,8 @@
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes): router logit = fp32 rounding of an fp64 pairwise sum of the
  * exact products; sigmoid evaluated in fp64 and rounded to fp32; ties in the
- * selection key go to the smaller expert id; hash-routed weights are 1/k;
+ * selection key go to the smaller expert id; hash-routed weights are 1/k (or,
+ * in the score-weighted variant, the renormalised router scores);
  * quantizer d = amax/127, q = rint(x * (1/d)) clamped to +-127; h is
  * quantized again before the down projection; the combine weight multiplies
  * the expert output after the down projection; the shared expert has weight 1.
@@ -140,20 +141,40 @@ void orc_route_learned(const float *logits, const float *bias, int32_t T, int32_
     free(taken);
 }
 
-/* a2 — hash selection: the token's table row in table order, weights 1/k. */
-int orc_route_hash(const int32_t *token_ids, const int32_t *table, int32_t vocab, int32_t T, int32_t E,
-                   int32_t k, int32_t *ids, float *w) {
+/* a2 — hash selection: the first k entries of the token's table row (rows of
+ * table_k >= k entries; keeping fewer than the row holds is the reduced top-k
+ * of "DeepSeek V4 Flash — DFlash Integration", Monolithic HIP,
+ * --ds4-expert-top-k), in table order, weights 1/k. */
+int orc_route_hash(const int32_t *token_ids, const int32_t *table, int32_t vocab, int32_t table_k, int32_t T,
+                   int32_t E, int32_t k, int32_t *ids, float *w) {
+    if (k < 1 || table_k < k) return -1;
     for (int32_t t = 0; t < T; ++t) {
         int32_t id = token_ids[t];
         if (id < 0 || id >= vocab) return -1;
         for (int32_t j = 0; j < k; ++j) {
-            int32_t e = table[(int64_t)id * k + j];
+            int32_t e = table[(int64_t)id * table_k + j];
             if (e < 0 || e >= E) return -1;
             for (int32_t i = 0; i < j; ++i)
-                if (table[(int64_t)id * k + i] == e) return -1;
+                if (table[(int64_t)id * table_k + i] == e) return -1;
             ids[(int64_t)t * k + j] = e;
             w[(int64_t)t * k + j] = 1.0f / (float)k;
         }
+    }
+    return 0;
+}
+
+/* a2 — score-weighted hash selection: the experts of orc_route_hash, each
+ * weighted by its router score s = sigmoid(logit) renormalised over the kept
+ * experts: S = sum of their scores in table order (fp32), w_j = s_j / S (the
+ * renormalisation of --ds4-expert-top-k applied to table-chosen experts). */
+int orc_route_hash_scored(const int32_t *token_ids, const int32_t *table, int32_t vocab, int32_t table_k,
+                          const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids, float *w) {
+    if (orc_route_hash(token_ids, table, vocab, table_k, T, E, k, ids, w) != 0) return -1;
+    for (int32_t t = 0; t < T; ++t) {
+        float S = 0.0f;
+        for (int32_t j = 0; j < k; ++j) S += orc_sigmoid(logits[(int64_t)t * E + ids[(int64_t)t * k + j]]);
+        for (int32_t j = 0; j < k; ++j)
+            w[(int64_t)t * k + j] = orc_sigmoid(logits[(int64_t)t * E + ids[(int64_t)t * k + j]]) / S;
     }
     return 0;
 }
@@ -287,17 +308,21 @@ int orc_forward(const orc_shape *s, const orc_weights *wt, const float *x, const
     const int32_t H = s->hidden, E = s->n_experts, k = s->top_k, F = s->ffn;
     if (T < 0 || k < 1 || k > E || H % 32 || F % 32) return -1;
     if (s->routed_fmt == ORC_FMT_Q2 && (H % 256 || F % 256)) return -1;
-    if (s->route == ORC_ROUTE_LEARNED && !is_pow2(H)) return -1;
+    const int32_t table_k = s->table_k ? s->table_k : k;
+    if (s->route != ORC_ROUTE_HASH && !is_pow2(H)) return -1;
     int32_t *ids_ = ids ? ids : (int32_t *)malloc(sizeof(int32_t) * (size_t)T * k + 1);
     float *w_ = w ? w : (float *)malloc(sizeof(float) * (size_t)T * k + 1);
     int rc = 0;
-    if (s->route == ORC_ROUTE_LEARNED) {
+    if (s->route == ORC_ROUTE_HASH) {
+        rc = orc_route_hash(token_ids, wt->table, wt->vocab, table_k, T, E, k, ids_, w_);
+    } else {
         float *l = logits ? logits : (float *)malloc(sizeof(float) * (size_t)T * E + 1);
         orc_router_logits(x, wt->router_w, T, E, H, l);
-        orc_route_learned(l, wt->router_b, T, E, k, ids_, w_, NULL);
+        if (s->route == ORC_ROUTE_LEARNED)
+            orc_route_learned(l, wt->router_b, T, E, k, ids_, w_, NULL);
+        else
+            rc = orc_route_hash_scored(token_ids, wt->table, wt->vocab, table_k, l, T, E, k, ids_, w_);
         if (!logits) free(l);
-    } else {
-        rc = orc_route_hash(token_ids, wt->table, wt->vocab, T, E, k, ids_, w_);
     }
     if (rc == 0) {
         const int32_t fmt = s->routed_fmt;

@@ -20,7 +20,7 @@ extern "C" {
 #endif
 
 enum { ORC_FMT_Q8 = 1, ORC_FMT_Q2 = 2 };
-enum { ORC_ROUTE_LEARNED = 1, ORC_ROUTE_HASH = 2 };
+enum { ORC_ROUTE_LEARNED = 1, ORC_ROUTE_HASH = 2, ORC_ROUTE_HASH_SCORED = 3 };
 
 typedef struct {
     int32_t hidden;     /* H */
@@ -29,15 +29,16 @@ typedef struct {
     int32_t ffn;        /* F (routed and shared) */
     int32_t has_shared; /* 0 or 1 */
     int32_t routed_fmt; /* ORC_FMT_Q8 / ORC_FMT_Q2 (shared is always Q8) */
-    int32_t route;      /* ORC_ROUTE_LEARNED / ORC_ROUTE_HASH */
+    int32_t route;      /* ORC_ROUTE_LEARNED / ORC_ROUTE_HASH / ORC_ROUTE_HASH_SCORED */
+    int32_t table_k;    /* entries per hash-table row (0: top_k); the first top_k are kept */
 } orc_shape;
 
 /* Canonical weights: banks of E matrices (gate/up [F][H], down [H][F]) and the
  * shared expert's three Q8 matrices, in the storage formats of moe_oracle.c. */
 typedef struct {
-    const float *router_w;   /* [E][H] fp32 (learned) */
-    const float *router_b;   /* [E] fp32 or NULL */
-    const int32_t *table;    /* [vocab][k] (hash) */
+    const float *router_w;   /* [E][H] fp32 (learned, hash_scored) */
+    const float *router_b;   /* [E] fp32 or NULL (learned) */
+    const int32_t *table;    /* [vocab][table_k] (hash, hash_scored) */
     int32_t vocab;
     const uint8_t *gate, *up, *down;
     const uint8_t *sh_gate, *sh_up, *sh_down;
@@ -53,9 +54,14 @@ float orc_sigmoid(float l);
 /* a2: learned selection -> ids [T][k], weights [T][k]; scores [T][E] optional */
 void orc_route_learned(const float *logits, const float *bias, int32_t T, int32_t E, int32_t k,
                        int32_t *ids, float *w, float *scores);
-/* a2: hash selection; returns 0, or -1 for an out-of-range id or table entry */
-int orc_route_hash(const int32_t *token_ids, const int32_t *table, int32_t vocab, int32_t T, int32_t E,
-                   int32_t k, int32_t *ids, float *w);
+/* a2: hash selection from rows of table_k entries (first k kept), weights 1/k;
+ * returns 0, or -1 for an out-of-range id or table entry or a repeated expert */
+int orc_route_hash(const int32_t *token_ids, const int32_t *table, int32_t vocab, int32_t table_k, int32_t T,
+                   int32_t E, int32_t k, int32_t *ids, float *w);
+/* a2: hash selection as above, weights = the kept experts' router scores
+ * renormalised to sum to one (summed in table order) */
+int orc_route_hash_scored(const int32_t *token_ids, const int32_t *table, int32_t vocab, int32_t table_k,
+                          const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids, float *w);
 /* a3: quantize n values (n % 32 == 0) into int8 codes and fp32 block scales */
 void orc_quantize(const float *x, int64_t n, int8_t *q, float *d);
 /* a4: stable counting sort of the T*k (token, slot) pairs by expert */

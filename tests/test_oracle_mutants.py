@@ -45,6 +45,11 @@ MUTANTS = {
                           "double we = slot >= 0 ? (double)w_[(int64_t)t * k + (k - 1 - slot)] : 0.0;"),
     "bias_ignored": ("key[e] = s[e] + (bias ? bias[e] : 0.0f);", "key[e] = s[e];"),
     "hash_reversed": ("ids[(int64_t)t * k + j] = e;", "ids[(int64_t)t * k + (k - 1 - j)] = e;"),
+    "hash_row_stride": ("int32_t e = table[(int64_t)id * table_k + j];", "int32_t e = table[(int64_t)id * k + j];"),
+    "hash_scored_unnormalised": ("ids[(int64_t)t * k + j]]) / S;", "ids[(int64_t)t * k + j]]);"),
+    "hash_scored_term_dropped": ("for (int32_t j = 0; j < k; ++j) S += orc_sigmoid(",
+                                 "for (int32_t j = 1; j < k; ++j) S += orc_sigmoid("),
+    "hash_scored_equal_weights": ("            rc = orc_route_hash_scored(", "            rc = orc_route_hash(token_ids, wt->table, wt->vocab, table_k, T, E, k, ids_, w_); (void)("),
     "f16_exponent": ("else v = ldexp((double)(1024 + m), e - 25);", "else v = ldexp((double)(1024 + m), e - 24);"),
     "block_sum_index": ("acc += (int32_t)(int8_t)row[b * 34 + 2 + j] * (int32_t)aq[b * 32 + j];",
                         "acc += (int32_t)(int8_t)row[b * 34 + 2 + j] * (int32_t)aq[b * 32 + (j ^ 1)];"),

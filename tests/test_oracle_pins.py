@@ -193,6 +193,93 @@ def test_route_hash_table_rows_and_rejects():
         oracle.route_hash(np.array([4], np.int32), bad, 256)
 
 
+def test_route_hash_reduced_keeps_the_row_prefix():
+    """Rows of 6 entries of which k are kept (reduced top-k): the ids are the
+    first k table entries in table order, the weights 1/k."""
+    table = ms.distinct_rows(1000, 6, 256, seed=6, tag=99)
+    tok = np.array([0, 999, 17, 17, 512, 3], np.int32)
+    for k in (1, 4, 6):
+        ids, w = oracle.route_hash(tok, table, 256, k=k)
+        assert np.array_equal(ids, table[tok, :k])
+        assert np.all(w == np.float32(1) / np.float32(k))
+    with pytest.raises(ValueError):
+        oracle.route_hash(tok, table, 256, k=7)
+
+
+def test_route_hash_scored_equal_scores_give_equal_weights():
+    """Zero logits: every score is 1/2, the sum is k/2 exactly, so the
+    renormalised weights are exactly 1/k (closed form)."""
+    table = ms.distinct_rows(300, 6, 64, seed=7, tag=99)
+    tok = np.arange(0, 300, 7, dtype=np.int32)
+    for k in (3, 6):
+        ids, w = oracle.route_hash_scored(tok, table, np.zeros((len(tok), 64), np.float32), k=k)
+        assert np.array_equal(ids, table[tok, :k])
+        assert np.all(w == np.float32(1) / np.float32(k))
+
+
+def test_route_hash_scored_matches_learned_on_the_same_experts():
+    """A table row holding the learned top-k (rank order) is weighted exactly
+    as the learned router weights it: same scores, same summation order."""
+    rng = np.random.default_rng(23)
+    T, E, k = 40, 32, 6
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    ids_l, w_l, _ = oracle.route_learned(logits, bias, k)
+    ids_h, w_h = oracle.route_hash_scored(np.arange(T, dtype=np.int32), np.ascontiguousarray(ids_l), logits)
+    assert np.array_equal(ids_h, ids_l)
+    assert np.array_equal(w_h.view(np.uint32), w_l.view(np.uint32))
+
+
+def test_route_hash_scored_weights_are_renormalised_scores():
+    """Weights sum to one, follow the ratios of the sigmoid scores and never
+    decrease with the logit (384 experts, rows of 8, 4 or 8 kept)."""
+    rng = np.random.default_rng(24)
+    table = ms.distinct_rows(500, 8, 384, seed=8, tag=99)
+    tok = rng.integers(0, 500, 64).astype(np.int32)
+    logits = rng.standard_normal((64, 384)).astype(np.float32)
+    for k in (4, 8):
+        ids, w = oracle.route_hash_scored(tok, table, logits, k=k)
+        assert np.array_equal(ids, table[tok, :k])
+        for t in range(64):
+            assert abs(float(np.sum(w[t], dtype=np.float64)) - 1.0) <= k * 2.0 ** -23
+            lg = logits[t, ids[t]]
+            order = np.argsort(lg, kind="stable")
+            assert np.all(np.diff(w[t][order]) >= 0)
+            sc = 1.0 / (1.0 + np.exp(-lg.astype(np.float64)))
+            np.testing.assert_allclose(w[t] / w[t][0], sc / sc[0], rtol=1e-6)
+
+
+def test_route_learned_reduced_top_k_is_a_prefix():
+    """Keeping the N highest-ranked of the top 6 (reduced top-k) is the top-N:
+    the same leading ids, weights renormalised over the kept experts."""
+    rng = np.random.default_rng(25)
+    T, E = 50, 256
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    ids6, w6, _ = oracle.route_learned(logits, bias, 6)
+    for n in (1, 4):
+        ids_n, w_n, _ = oracle.route_learned(logits, bias, n)
+        assert np.array_equal(ids_n, ids6[:, :n])
+        for t in range(T):
+            assert abs(float(np.sum(w_n[t], dtype=np.float64)) - 1.0) <= n * 2.0 ** -23
+            np.testing.assert_allclose(w_n[t] / w_n[t][0], w6[t, :n] / w6[t, 0], rtol=1e-6)
+
+
+def test_route_learned_384_experts_top8_bruteforce():
+    """The 384-expert sigmoid top-8 shape: the selection is a brute-force
+    ranking of key = fp32 sigmoid + bias (larger first, ties to the smaller id)."""
+    rng = np.random.default_rng(26)
+    T, E, k = 24, 384, 8
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    logits[:, 200], bias[200] = logits[:, 7], bias[7]     # exact ties between experts 7 and 200
+    ids, _, _ = oracle.route_learned(logits, bias, k)
+    for t in range(T):
+        sig = (1.0 / (1.0 + np.exp(-logits[t].astype(np.float64)))).astype(np.float32)
+        key = [np.float32(sig[e]) + np.float32(bias[e]) for e in range(E)]
+        assert list(ids[t]) == brute_topk(key, k)
+
+
 # -------------------------------------------------------- a3: quantizer ---
 
 def test_quantizer_properties():
@@ -295,13 +382,26 @@ def test_sort_pairs_is_stable_counting_sort():
 
 # ------------------------------------------------------ whole-layer pins ---
 
-@pytest.mark.parametrize("k", [2, 4])
-def test_dense_masked_equals_routed_bitwise(k):
-    cfg = ms.CONFIGS["tiny"].with_(top_k=k)
+@pytest.mark.parametrize("k,route", [(2, "learned"), (4, "learned"), (3, "hash_scored")])
+def test_dense_masked_equals_routed_bitwise(k, route):
+    cfg = ms.CONFIGS["tiny"].with_(top_k=k, route=route, vocab=97, table_k=5 if route != "learned" else 0)
     inp = ms.make_inputs(cfg)
     routed = oracle.forward(cfg, inp)
     dense = oracle.forward(cfg, inp, dense=True)
     assert np.array_equal(routed["out"].view(np.uint32), dense["out"].view(np.uint32))
+
+
+def test_score_weighted_hash_layer_uses_its_table_and_router():
+    """Layer wiring of the score-weighted variant with rows of 6, 4 kept: ids
+    from the table prefix, weights from route_hash_scored on the router logits."""
+    cfg = ms.CONFIGS["tiny"].with_(route="hash_scored", top_k=4, table_k=6, vocab=200, tokens=9)
+    inp = ms.make_inputs(cfg)
+    r = oracle.forward(cfg, inp)
+    lg = oracle.router_logits(inp["x"], inp["router_w"])
+    assert np.array_equal(r["logits"].view(np.uint32), lg.view(np.uint32))
+    ids, w = oracle.route_hash_scored(inp["token_ids"], inp["hash_table"], lg, k=4)
+    assert np.array_equal(r["ids"], inp["hash_table"][inp["token_ids"], :4]) and np.array_equal(r["ids"], ids)
+    assert np.array_equal(r["w"].view(np.uint32), w.view(np.uint32))
 
 
 def test_hash_layer_reproduces_its_table():
