@@ -128,18 +128,19 @@ def stage_model(cfg, qr, u_avg):
     T, H, E, k, F = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn
     fmt = qr.FMT[cfg.routed_fmt]
     sh = 1 if cfg.shared else 0
-    learned = cfg.route == "learned"
+    has_router = cfg.route != "hash"     # logits, scores and keys are computed (learned, hash_scored)
+    table = T * k * 4 if cfg.route != "learned" else 0   # hash-table entries read
     mq8_gu, mq8_dn = qr.matrix_bytes(qr.FMT_Q8, F, H), qr.matrix_bytes(qr.FMT_Q8, H, F)
     mr_gu, mr_dn = qr.matrix_bytes(fmt, F, H), qr.matrix_bytes(fmt, H, F)
     Pr, P = T * k, T * k + sh * T
     x32 = T * H * 4
     xq = T * H + T * (H // 32) * 4
     hq = lambda n: n * F + n * (F // 32) * 4
-    router = E * H * 4 if learned else T * k * 4
-    rout = 3 * T * E * 4 if learned else 0
+    router = (E * H * 4 if has_router else 0) + table
+    rout = 3 * T * E * 4 if has_router else 0
     st = {}
     if T <= 32:
-        sel = (2 * T * E * 4 if learned else T * 4) + T * k * 12
+        sel = (2 * T * E * 4 if has_router else T * 4) + T * k * 12
         if T == 1:  # selection and the shared expert's gate/up run in the gate/up kernel
             st["route"] = router + x32 + xq + rout
             st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P) + sel
@@ -155,15 +156,15 @@ def stage_model(cfg, qr, u_avg):
             st["combine"] = P * H * 4 + x32
     else:
         st["quant"] = x32 + xq
-        if learned:
+        if has_router:
             st["logits"] = router + x32 + rout
-        st["select"] = (2 * T * E * 4 if learned else T * 4) + T * k * 8
+        st["select"] = (2 * T * E * 4 if has_router else T * 4) + T * k * 8
         st["sort"] = T * k * 4 * 3
         st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P)
         st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + P * H * 4
         st["combine"] = P * H * 4 + x32
     ops = {"gateup": 2 * P * 2 * F * H, "down": 2 * P * H * F}
-    layer = (u_avg * (2 * mr_gu + mr_dn) + sh * (2 * mq8_gu + mq8_dn) + (router if learned else 0) + 2 * x32)
+    layer = (u_avg * (2 * mr_gu + mr_dn) + sh * (2 * mq8_gu + mq8_dn) + (E * H * 4 if has_router else 0) + 2 * x32)
     return {"stages": {s: {"bytes": b, "ops": ops.get(s)} for s, b in st.items()}, "layer_bytes": layer}
 
 
@@ -279,7 +280,7 @@ def main():
     t_setup = time.time()
     inp = ms.make_inputs(cfg)
     layer = qr.MoELayer(H, E, k, F, cfg.shared, cfg.routed_fmt, cfg.route,
-                        cfg.vocab if cfg.route == "hash" else 0).load(inp)
+                        cfg.vocab if cfg.route != "learned" else 0, table_k=cfg.table_k).load(inp)
     R = max(1, args.replicas)
     reps = []
     for r in range(R):
@@ -293,7 +294,7 @@ def main():
     n_steps = args.warmup + G
     xs = torch.from_numpy(ms.extra_tokens(cfg, n_steps * T)).to(dev).reshape(n_steps, T, H)
     toks = None
-    if cfg.route == "hash":
+    if cfg.route != "learned":
         toks = torch.from_numpy(ms.uniform_i32(n_steps * T, 0, cfg.vocab - 1, cfg.seed,
                                                ms.TAG["token_ids"])).to(dev).reshape(n_steps, T)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -403,7 +404,7 @@ def main():
         n_host = max(4096, 64 * T)
         xs_host = ms.extra_tokens(cfg, n_host)
         tk_host = (ms.uniform_i32(n_host, 0, cfg.vocab - 1, cfg.seed, ms.TAG["token_ids"])
-                   if cfg.route == "hash" else None)
+                   if cfg.route != "learned" else None)
         n_tok, spent, batch = 0, 0.0, max(threads, 1)
         while spent < args.cpu_seconds and n_tok + batch <= xs_host.shape[0]:
             sel = slice(n_tok, n_tok + batch)

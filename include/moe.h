@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_TOKENS 16384 /* tokens per call; larger batches are refused, not split */
 
 typedef enum moe_status {
@@ -73,11 +73,20 @@ typedef enum moe_status {
  * Forward calls read weights only in the PACKED layout that moe_pack_weights
  * produces from the canonical one (same byte count). */
 enum { MOE_FMT_Q8_32 = 1, MOE_FMT_Q2_256 = 2 };
-enum { MOE_ROUTE_LEARNED = 1, MOE_ROUTE_HASH = 2 };
+/* Routing (a2).  LEARNED: sigmoid scores of the router logits, the top_k
+ * largest score + bias, weights = scores renormalised over the kept experts.
+ * HASH: the first top_k entries of the token's row of a fixed table, weights
+ * 1/top_k.  HASH_SCORED: the table's experts weighted by their router scores
+ * renormalised over the kept experts (summed in table order).  Keeping fewer
+ * experts than a table row holds (top_k < table_k), or a smaller top_k for
+ * the learned router, is the reduced top-k of "DeepSeek V4 Flash — DFlash
+ * Integration", Monolithic HIP (--ds4-expert-top-k). */
+enum { MOE_ROUTE_LEARNED = 1, MOE_ROUTE_HASH = 2, MOE_ROUTE_HASH_SCORED = 3 };
 
 /* Layer shape.  Supported: hidden H and ffn F powers of two in [128, 4096]
  * (Q8_32; Q2_256 needs [512, 4096]); 1 <= top_k <= 8; top_k <= n_experts
- * <= 1024; vocab >= 1 for hash routing. */
+ * <= 1024; for the two hash routes vocab >= 1 and table_k == 0 (rows of
+ * top_k entries) or top_k <= table_k <= 8. */
 typedef struct moe_shape {
     int32_t hidden;     /* H */
     int32_t n_experts;  /* E routed experts */
@@ -87,13 +96,14 @@ typedef struct moe_shape {
     int32_t routed_fmt; /* MOE_FMT_* of the routed experts */
     int32_t route;      /* MOE_ROUTE_* */
     int32_t vocab;      /* rows of the hash table (hash routing) */
+    int32_t table_k;    /* entries per hash-table row; 0 means top_k */
 } moe_shape;
 
 /* Layer weights, all device pointers, 16-byte aligned. */
 typedef struct moe_weights {
-    const float *router_w;     /* learned: [E][H] fp32 */
+    const float *router_w;     /* learned, hash_scored: [E][H] fp32 */
     const float *router_b;     /* learned: [E] fp32, or NULL for no bias */
-    const int32_t *hash_table; /* hash: [vocab][k] int32 expert ids */
+    const int32_t *hash_table; /* hash, hash_scored: [vocab][table_k] int32 expert ids */
     const void *gate;          /* packed bank of E matrices [F][H] in routed_fmt */
     const void *up;            /* packed bank of E matrices [F][H] in routed_fmt */
     const void *down;          /* packed bank of E matrices [H][F] in routed_fmt */
@@ -108,7 +118,7 @@ typedef struct moe_weights {
 typedef struct moe_debug {
     int32_t *ids;      /* [T][k] selected experts, rank order */
     float *w;          /* [T][k] combine weights */
-    float *logits;     /* [T][E] router logits (learned) */
+    float *logits;     /* [T][E] router logits (learned, hash_scored) */
     int8_t *xq;        /* [T][H] quantized x */
     float *xd;         /* [T][H/32] x block scales */
     int32_t *counts;   /* [E] pairs per expert */
@@ -146,11 +156,12 @@ int64_t moe_matrix_bytes(int32_t fmt, int64_t rows, int64_t cols);
 int moe_pack_weights(int32_t fmt, const void *canonical, void *packed, int64_t n_mats, int64_t rows, int64_t cols,
                      void *stream);
 
-/* Check a hash table on the device: every entry in [0, n_experts) and no
- * expert twice in a row.  Synchronises `stream`.  Needs a workspace of at
- * least 256 bytes.  Returns MOE_OK or MOE_ERR_BAD_TABLE with the first bad
- * row in *bad_row (host pointer, may be NULL). */
-int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t top_k, int32_t n_experts, void *workspace,
+/* Check a hash table [vocab][row_k] on the device (row_k = the shape's
+ * table_k, or top_k when that is 0; at most 8): every entry in
+ * [0, n_experts) and no expert twice in a row.  Synchronises `stream`.  Needs
+ * a workspace of at least 256 bytes.  Returns MOE_OK or MOE_ERR_BAD_TABLE
+ * with the first bad row in *bad_row (host pointer, may be NULL). */
+int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t row_k, int32_t n_experts, void *workspace,
                          size_t workspace_bytes, int32_t *bad_row, void *stream);
 
 /* Device workspace bytes a forward call with `tokens` tokens needs (0 when

@@ -26,9 +26,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 FMT_Q8, FMT_Q2 = 1, 2
-ROUTE_LEARNED, ROUTE_HASH = 1, 2
+ROUTE_LEARNED, ROUTE_HASH, ROUTE_HASH_SCORED = 1, 2, 3
 FMT = {"q8": FMT_Q8, "q2": FMT_Q2}
-ROUTE = {"learned": ROUTE_LEARNED, "hash": ROUTE_HASH}
+ROUTE = {"learned": ROUTE_LEARNED, "hash": ROUTE_HASH, "hash_scored": ROUTE_HASH_SCORED}
 STAGES = ["route", "quant", "logits", "select", "sort", "gateup", "down", "combine"]
 ALIGN = 256
 
@@ -44,7 +44,7 @@ class MoEError(RuntimeError):
 
 class Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("hidden", "n_experts", "top_k", "ffn", "has_shared", "routed_fmt", "route", "vocab")]
+                ("hidden", "n_experts", "top_k", "ffn", "has_shared", "routed_fmt", "route", "vocab", "table_k")]
 
 
 class Weights(ctypes.Structure):
@@ -111,9 +111,10 @@ def matrix_bytes(fmt: int, rows: int, cols: int) -> int:
     return _lib.moe_matrix_bytes(fmt, rows, cols)
 
 
-def make_shape(hidden, n_experts, top_k, ffn, has_shared=True, routed_fmt="q8", route="learned", vocab=0) -> Shape:
+def make_shape(hidden, n_experts, top_k, ffn, has_shared=True, routed_fmt="q8", route="learned", vocab=0,
+               table_k=0) -> Shape:
     return Shape(hidden, n_experts, top_k, ffn, 1 if has_shared else 0, FMT[routed_fmt] if isinstance(routed_fmt, str)
-                 else routed_fmt, ROUTE[route] if isinstance(route, str) else route, vocab)
+                 else routed_fmt, ROUTE[route] if isinstance(route, str) else route, vocab, table_k)
 
 
 def workspace_bytes(shape: Shape, tokens: int) -> int:
@@ -194,4 +195,5 @@ from .layer import MoELayer  # noqa: E402
 
 __all__ = ["MoELayer", "MoEError", "Shape", "Weights", "Debug", "Profiler", "make_shape", "workspace_bytes",
            "pack_weights", "layer_forward", "workspace_init", "workspace_flags", "check_hash_table", "matrix_bytes",
-           "abi_version", "FMT_Q8", "FMT_Q2", "ROUTE_LEARNED", "ROUTE_HASH", "EXPORTED", "LIB_PATH"]
+           "abi_version", "FMT_Q8", "FMT_Q2", "ROUTE_LEARNED", "ROUTE_HASH", "ROUTE_HASH_SCORED", "EXPORTED",
+           "LIB_PATH"]

@@ -32,10 +32,14 @@ inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int validate_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARG;
     if (s->routed_fmt != MOE_FMT_Q8_32 && s->routed_fmt != MOE_FMT_Q2_256) return MOE_ERR_INVALID_ARG;
-    if (s->route != MOE_ROUTE_LEARNED && s->route != MOE_ROUTE_HASH) return MOE_ERR_INVALID_ARG;
+    if (s->route != MOE_ROUTE_LEARNED && s->route != MOE_ROUTE_HASH && s->route != MOE_ROUTE_HASH_SCORED)
+        return MOE_ERR_INVALID_ARG;
     if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_INVALID_ARG;
     if (s->top_k < 1 || s->n_experts < s->top_k) return MOE_ERR_INVALID_ARG;
-    if (s->route == MOE_ROUTE_HASH && s->vocab < 1) return MOE_ERR_INVALID_ARG;
+    if (s->route != MOE_ROUTE_LEARNED) {
+        if (s->vocab < 1) return MOE_ERR_INVALID_ARG;
+        if (s->table_k != 0 && (s->table_k < s->top_k || s->table_k > 8)) return MOE_ERR_INVALID_ARG;
+    }
     if (s->top_k > 8 || s->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
     const int lo = s->routed_fmt == MOE_FMT_Q2_256 ? 512 : 128;
     if (!pow2(s->hidden) || !pow2(s->ffn) || s->hidden < lo || s->ffn < lo || s->hidden > 4096 || s->ffn > 4096)
@@ -151,9 +155,10 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
     if (tokens > MOE_MAX_TOKENS) return MOE_ERR_TOO_MANY_TOKENS;
     if (tokens == 0) return MOE_OK;  // empty batch: nothing is read or written, buffers may be NULL
     if (!wts || !x || !out || !workspace) return MOE_ERR_INVALID_ARG;
-    const bool learned = shape->route == MOE_ROUTE_LEARNED;
-    if (learned && !wts->router_w) return MOE_ERR_INVALID_ARG;
-    if (!learned && (!wts->hash_table || !token_ids)) return MOE_ERR_INVALID_ARG;
+    const bool router = shape->route != MOE_ROUTE_HASH;     // logits are computed
+    const bool hashed = shape->route != MOE_ROUTE_LEARNED;  // experts come from the table
+    if (router && !wts->router_w) return MOE_ERR_INVALID_ARG;
+    if (hashed && (!wts->hash_table || !token_ids)) return MOE_ERR_INVALID_ARG;
     if (!wts->gate || !wts->up || !wts->down) return MOE_ERR_INVALID_ARG;
     if (shape->has_shared && (!wts->sh_gate || !wts->sh_up || !wts->sh_down)) return MOE_ERR_INVALID_ARG;
     if (!shape->has_shared && (wts->sh_gate || wts->sh_up || wts->sh_down)) return MOE_ERR_INVALID_ARG;
@@ -177,7 +182,8 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
     LayerArgs a{};
     a.d = Dims{(int32_t)T, shape->hidden, shape->n_experts, shape->top_k, shape->ffn, shape->has_shared,
                shape->routed_fmt, shape->route, shape->vocab,
-               (int32_t)(T * shape->top_k + (shape->has_shared ? T : 0))};
+               (int32_t)(T * shape->top_k + (shape->has_shared ? T : 0)),
+               hashed && shape->table_k ? shape->table_k : shape->top_k};
     a.wt = Weights{wts->router_w, wts->router_b, wts->hash_table, (const uint8_t *)wts->gate,
                    (const uint8_t *)wts->up, (const uint8_t *)wts->down, (const uint8_t *)wts->sh_gate,
                    (const uint8_t *)wts->sh_up, (const uint8_t *)wts->sh_down};
@@ -221,7 +227,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
         const int64_t tiles = mfma ? max_groups(shape, T, kMfmaTile) : mg;
         a.group_tok = mfma ? kMfmaTile : kVecTok;
         run(MOE_STAGE_QUANT, [&] { return launch_quant(a, s); });
-        if (learned) run(MOE_STAGE_LOGITS, [&] { return launch_logits(a, s); });
+        if (router) run(MOE_STAGE_LOGITS, [&] { return launch_logits(a, s); });
         run(MOE_STAGE_SELECT, [&] { return launch_select(a, s); });
         run(MOE_STAGE_SORT, [&] { return launch_sort(a, s); });
         if (mfma) {
@@ -240,7 +246,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
         };
         cp(dbg->ids, a.ws.ids, T * k * 4);
         cp(dbg->w, a.ws.w, T * k * 4);
-        if (learned) cp(dbg->logits, a.ws.logits, T * E * 4);
+        if (router) cp(dbg->logits, a.ws.logits, T * E * 4);
         cp(dbg->xq, a.ws.xq, T * H);
         cp(dbg->xd, a.ws.xd, T * (H / 32) * 4);
         cp(dbg->counts, a.ws.counts, E * 4);
@@ -294,14 +300,14 @@ int moe_pack_weights(int32_t fmt, const void *canonical, void *packed, int64_t n
     return hip_status(err);
 }
 
-int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t top_k, int32_t n_experts, void *workspace,
+int moe_check_hash_table(const int32_t *table, int32_t vocab, int32_t row_k, int32_t n_experts, void *workspace,
                          size_t workspace_bytes, int32_t *bad_row, void *stream) {
-    if (!table || !workspace || vocab < 1 || top_k < 1 || top_k > 8 || n_experts < top_k) return MOE_ERR_INVALID_ARG;
+    if (!table || !workspace || vocab < 1 || row_k < 1 || row_k > 8 || n_experts < row_k) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < 256 || !aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     int32_t *res = (int32_t *)workspace + (kCtlWords - 1);  // scratch word of the ctl area, never a counter
     if (workspace_bytes < (size_t)kCtlWords * 4) res = (int32_t *)workspace;
-    hipError_t err = launch_check_table(table, vocab, top_k, n_experts, res, s);
+    hipError_t err = launch_check_table(table, vocab, row_k, n_experts, res, s);
     int32_t host = 0;
     if (err == hipSuccess) err = hipMemcpyAsync(&host, res, 4, hipMemcpyDeviceToHost, s);
     if (err == hipSuccess) err = hipStreamSynchronize(s);

@@ -17,7 +17,7 @@ constexpr int kVecTok = 8;          // tokens per work group of the VALU expert 
 constexpr int kVecRows = 32;        // weight rows per workgroup of the VALU expert kernels (= one h block)
 constexpr int kDecodeMaxT = 32;     // batches up to this size take the decode path
 constexpr int kFmtQ8 = 1, kFmtQ2 = 2;
-constexpr int kRouteLearned = 1, kRouteHash = 2;
+constexpr int kRouteLearned = 1, kRouteHash = 2, kRouteHashScored = 3;
 
 // ctl[] words of the workspace
 enum : int { kCtlGroups = 1, kCtlFlags = 2, kCtlMagic = 3 };
@@ -46,6 +46,7 @@ __host__ __device__ inline int64_t mat_bytes(int fmt, int64_t R, int64_t K) {
 struct Dims {
     int32_t T, H, E, k, F, has_shared, fmt, route, vocab;
     int32_t P;  // pairs including the shared expert's: T*k + T*has_shared
+    int32_t table_k;  // entries per hash-table row (>= k)
 };
 
 // Workspace pointers (device).

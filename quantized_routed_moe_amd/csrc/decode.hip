@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_le
         const int nblk = d.T * (H / 32);
         for (int b = blockIdx.x * 256 + tid; b < nblk; b += n_lead * 256)
             quant_one_block(a.x, a.ws.xq, a.ws.xd, d.fmt == kFmtQ2 ? a.ws.xs16 : nullptr, b);
-        if (d.route != kRouteLearned) return;
+        if (d.route == kRouteHash) return;  // no router
         const int nlog = d.T * d.E;
         if constexpr (H >= 256) {
             // one logit per workgroup; wave w sums elements [w*H/4, (w+1)*H/4)
@@ -129,8 +129,9 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
             select_keys_wave(a.ws.keys + (int64_t)t * d.E, a.ws.scores + (int64_t)t * d.E, d.E, d.k, rs.ids + t * d.k,
                              rs.w + t * d.k, lane);
         else
-            select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.E, d.k, rs.ids + t * d.k, rs.w + t * d.k,
-                             a.ws.ctl + kCtlFlags, lane);
+            select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.table_k, d.E, d.k, rs.ids + t * d.k,
+                             rs.w + t * d.k, a.ws.ctl + kCtlFlags,
+                             d.route == kRouteHashScored ? a.ws.scores + (int64_t)t * d.E : nullptr, lane);
     }
     __syncthreads();
     if (tid < P) {
@@ -241,8 +242,9 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
         if (d.route == kRouteLearned)
             select_keys_regs(a.ws.keys, a.ws.scores, d.E, d.k, id, w, lane);
         else
-            select_hash_regs(a.token_ids, a.wt.table, 0, d.vocab, d.E, d.k, id, w,
-                             publish ? a.ws.ctl + kCtlFlags : &ss.flags, lane);
+            select_hash_regs(a.token_ids, a.wt.table, 0, d.vocab, d.table_k, d.E, d.k, id, w,
+                             publish ? a.ws.ctl + kCtlFlags : &ss.flags,
+                             d.route == kRouteHashScored ? a.ws.scores : nullptr, lane);
         // lane j < k holds rank slot j: order the slots by (expert, slot) in
         // registers, then the distinct experts in ascending id
         const int k = d.k;
@@ -460,7 +462,7 @@ static hipError_t front_h(const LayerArgs &a, hipStream_t s) {
     const Dims &d = a.d;
     const int nq = (d.T * (H / 32) + 255) / 256;
     int n_lead = nq;
-    if (d.route == kRouteLearned) {
+    if (d.route != kRouteHash) {
         const int nl = H >= 256 ? d.T * d.E : (d.T * d.E + 3) / 4;
         n_lead = nl > nq ? nl : nq;
     }

@@ -176,10 +176,13 @@ __device__ __forceinline__ void select_keys_wave(const float *__restrict__ krow,
     }
 }
 
-// Lane j < k receives the token's j-th table entry (clamped and flagged when out of range) and 1/k.
+// Lane j < k receives the j-th entry of the token's table row (rows of
+// row_k >= k entries; clamped and flagged when out of range) and its weight:
+// 1/k, or with srow (the token's sigmoid scores) the score renormalised over
+// the k kept experts, S summed in table order (lane order).
 __device__ __forceinline__ void select_hash_regs(const int32_t *__restrict__ token_ids, const int32_t *__restrict__ table,
-                                                 int t, int vocab, int E, int k, int &id_out, float &w_out,
-                                                 int32_t *flags, int lane) {
+                                                 int t, int vocab, int row_k, int E, int k, int &id_out, float &w_out,
+                                                 int32_t *flags, const float *__restrict__ srow, int lane) {
     int id = token_ids[t];
     if (id < 0 || id >= vocab) {
         if (lane == 0) atomicOr(flags, 1);
@@ -188,7 +191,7 @@ __device__ __forceinline__ void select_hash_regs(const int32_t *__restrict__ tok
     id_out = 0;
     w_out = 0.0f;
     if (lane < k) {
-        int e = table[(int64_t)id * k + lane];
+        int e = table[(int64_t)id * row_k + lane];
         if (e < 0 || e >= E) {
             atomicOr(flags, 2);
             e = 0;
@@ -196,13 +199,22 @@ __device__ __forceinline__ void select_hash_regs(const int32_t *__restrict__ tok
         id_out = e;
         w_out = 1.0f / (float)k;
     }
+    if (srow) {
+        const float sc = lane < k ? srow[id_out] : 0.0f;
+        float S = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) S += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), j));
+        if (lane < k) w_out = sc / S;
+    }
 }
 
 __device__ void select_hash_wave(const int32_t *__restrict__ token_ids, const int32_t *__restrict__ table, int t,
-                                 int vocab, int E, int k, int32_t *ids_out, float *w_out, int32_t *flags, int lane) {
+                                 int vocab, int row_k, int E, int k, int32_t *ids_out, float *w_out, int32_t *flags,
+                                 const float *__restrict__ srow, int lane) {
     int id;
     float w;
-    select_hash_regs(token_ids, table, t, vocab, E, k, id, w, flags, lane);
+    select_hash_regs(token_ids, table, t, vocab, row_k, E, k, id, w, flags, srow, lane);
     if (lane < k) {
         ids_out[lane] = id;
         w_out[lane] = w;

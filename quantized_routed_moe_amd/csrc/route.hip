@@ -282,7 +282,8 @@ __device__ __forceinline__ void select_token(const LayerArgs &a, int t, int32_t 
     if (d.route == kRouteLearned)
         select_keys_wave(a.ws.keys + (int64_t)t * d.E, a.ws.scores + (int64_t)t * d.E, d.E, d.k, ids, w, lane);
     else
-        select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.E, d.k, ids, w, a.ws.ctl + kCtlFlags, lane);
+        select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.table_k, d.E, d.k, ids, w, a.ws.ctl + kCtlFlags,
+                         d.route == kRouteHashScored ? a.ws.scores + (int64_t)t * d.E : nullptr, lane);
 }
 
 __global__ __launch_bounds__(256) void select_kernel(LayerArgs a) {

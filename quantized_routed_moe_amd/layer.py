@@ -31,12 +31,12 @@ class MoELayer:
     """
 
     def __init__(self, hidden, n_experts, top_k, ffn, has_shared=True, routed_fmt="q8", route="learned", vocab=0,
-                 device="cuda"):
+                 device="cuda", table_k=0):
         self.device = torch.device(device)
         self.H, self.E, self.k, self.F = hidden, n_experts, top_k, ffn
-        self.routed_fmt, self.route, self.vocab = routed_fmt, route, vocab
+        self.routed_fmt, self.route, self.vocab, self.table_k = routed_fmt, route, vocab, table_k
         self.has_shared = has_shared
-        self.shape = make_shape(hidden, n_experts, top_k, ffn, has_shared, routed_fmt, route, vocab)
+        self.shape = make_shape(hidden, n_experts, top_k, ffn, has_shared, routed_fmt, route, vocab, table_k)
         self.router_w = self.router_b = self.hash_table = None
         self.gate = self.up = self.down = None
         self.sh_gate = self.sh_up = self.sh_down = None
@@ -58,14 +58,15 @@ class MoELayer:
         return dst
 
     def load(self, inp: dict) -> "MoELayer":
-        """Upload canonical tensors (numpy or CPU torch): router_w, router_b or hash_table,
-        gate/up/down banks and sh_gate/sh_up/sh_down."""
+        """Upload canonical tensors (numpy or CPU torch): router_w (learned, hash_scored),
+        router_b (learned), hash_table (hash routes), gate/up/down banks and
+        sh_gate/sh_up/sh_down."""
         fmt = FMT[self.routed_fmt]
-        if self.route == "learned":
+        if self.route != "hash":
             self.router_w = _upload(inp["router_w"], self.device)
-            if inp.get("router_b") is not None:
-                self.router_b = _upload(inp["router_b"], self.device)
-        else:
+        if self.route == "learned" and inp.get("router_b") is not None:
+            self.router_b = _upload(inp["router_b"], self.device)
+        if self.route != "learned":
             self.hash_table = _upload(inp["hash_table"], self.device)
         self.gate = self.pack_bank(inp["gate"], fmt, self.E, self.F, self.H)
         self.up = self.pack_bank(inp["up"], fmt, self.E, self.F, self.H)

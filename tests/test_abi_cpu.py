@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert qr.abi_version() == 1
+    assert qr.abi_version() == 2
     for st in range(-7, 1):
         assert L.moe_status_string(st) not in (None, b"unknown status")
     assert L.moe_status_string(-99) == b"unknown status"
@@ -56,9 +56,13 @@ def test_workspace_bytes_monotone_and_rejects_bad_shapes():
     assert all(b > 0 for b in sizes) and sizes == sorted(sizes)
     assert qr.workspace_bytes(s, 16385) == 0
     for bad in (dict(hidden=96), dict(hidden=8192), dict(ffn=64), dict(top_k=0), dict(top_k=9), dict(n_experts=4),
-                dict(n_experts=2048), dict(routed_fmt=3), dict(route=0), dict(route="hash", vocab=0),
-                dict(routed_fmt="q2", hidden=256)):
+                dict(n_experts=2048), dict(routed_fmt=3), dict(route=0), dict(route=4), dict(route="hash", vocab=0),
+                dict(route="hash_scored", vocab=0), dict(route="hash", vocab=10, table_k=5),
+                dict(route="hash_scored", vocab=10, table_k=9), dict(routed_fmt="q2", hidden=256)):
         assert qr.workspace_bytes(shape(**bad), 4) == 0, bad
+    for good in (dict(route="hash", vocab=10, table_k=6), dict(route="hash", vocab=10, top_k=4, table_k=8),
+                 dict(route="hash_scored", vocab=10), dict(n_experts=384, top_k=8)):
+        assert qr.workspace_bytes(shape(**good), 4) > 0, good
 
 
 FAKE = 1 << 20  # 16- and 256-byte aligned host integers: never dereferenced by the host checks
@@ -100,6 +104,10 @@ def test_forward_validation_codes():
     w3 = good_weights()
     w3.hash_table = None
     assert call_forward(hs, w3, tok=FAKE * 7) == INVALID
+    ss = shape(route="hash_scored", vocab=131072, top_k=4, table_k=6)
+    assert call_forward(ss, w2, tok=FAKE * 7) == INVALID                  # score-weighted hash needs the router
+    assert call_forward(ss, w3, tok=FAKE * 7) == INVALID                  # ... and the table
+    assert call_forward(ss, w, tok=None) == INVALID                       # ... and token ids
     assert call_forward(s, w, T=0) == OK                                  # empty batch: nothing to do
     assert L.moe_layer_forward(ctypes.byref(s), None, None, None, 0, None, None, 0, None) == OK
 

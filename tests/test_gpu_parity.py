@@ -40,7 +40,7 @@ def case(cfg):
         torch.cuda.empty_cache()
         inp = ms.make_inputs(cfg)
         layer = _qr().MoELayer(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared, cfg.routed_fmt, cfg.route,
-                               cfg.vocab if cfg.route == "hash" else 0).load(inp)
+                               cfg.vocab if cfg.route != "learned" else 0, table_k=cfg.table_k).load(inp)
         _cache[cfg] = (inp, layer)
     return _cache[cfg]
 
@@ -56,7 +56,7 @@ def run_gpu(cfg, inp, layer, x=None, tok=None, stride=0):
     x = inp["x"] if x is None else x
     xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     tt = None
-    if cfg.route == "hash":
+    if cfg.route != "learned":
         tok = inp["token_ids"] if tok is None else tok
         tt = torch.from_numpy(np.ascontiguousarray(tok)).cuda()
     r = layer.forward_debug(xt, tt, sum_row_stride=stride)
@@ -72,16 +72,19 @@ def check(cfg, inp, g, x=None, tok=None, rows=None, stride=0, name=""):
     """Compare GPU results g with the oracle; rows = tokens to run the full oracle on."""
     x = inp["x"] if x is None else x
     T, H, E, k, F = x.shape[0], cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn
-    if cfg.route == "hash":
+    if cfg.route != "learned":
         tok = inp["token_ids"] if tok is None else tok
     rows = np.arange(T) if rows is None else np.asarray(rows)
     # a1/a2: routing of every token, bit-exact
-    if cfg.route == "learned":
+    if cfg.route != "hash":
         lo = oracle.router_logits(x, inp["router_w"])
         assert np.array_equal(bits(g["logits"]), bits(lo)), "router logits differ"
+    if cfg.route == "learned":
         ids_o, w_o, _ = oracle.route_learned(lo, inp["router_b"], k)
+    elif cfg.route == "hash":
+        ids_o, w_o = oracle.route_hash(tok, inp["hash_table"], E, k=k)
     else:
-        ids_o, w_o = oracle.route_hash(tok, inp["hash_table"], E)
+        ids_o, w_o = oracle.route_hash_scored(tok, inp["hash_table"], lo, k=k)
     assert np.array_equal(g["ids"], ids_o), "expert selection differs"
     assert np.array_equal(bits(g["w"]), bits(w_o)), "combine weights differ"
     # a3: quantized x, bit-exact
@@ -92,7 +95,7 @@ def check(cfg, inp, g, x=None, tok=None, rows=None, stride=0, name=""):
     assert np.array_equal(g["counts"], c_o) and np.array_equal(g["offsets"], off_o)
     assert np.array_equal(g["perm"], perm_o), "token sort differs"
     # a5/a6: outputs of the sampled tokens
-    o = oracle.forward(cfg, inp, x=x[rows], token_ids=tok[rows] if cfg.route == "hash" else None)
+    o = oracle.forward(cfg, inp, x=x[rows], token_ids=tok[rows] if cfg.route != "learned" else None)
     out_g, out_o = g["out"][rows], o["out"]
     assert np.all(np.isfinite(out_g))
     scale = float(np.max(np.abs(out_o)))
@@ -155,6 +158,17 @@ SMALL = [
     ms.LayerConfig("q8_mfma_1024_T300", 1024, 16, 4, 512, 300, seed=26),
     ms.LayerConfig("q8_mfma_hash_T77", 512, 64, 6, 256, 77, route="hash", vocab=5000, seed=27),
     ms.LayerConfig("q8_mfma_noshared_T45", 256, 8, 3, 256, 45, shared=False, seed=28),
+    # routing variants: score-weighted hash, hash rows wider than top-k, 384 experts top-8
+    ms.LayerConfig("q8_hashscored_T1", 512, 32, 6, 256, 1, route="hash_scored", vocab=300, seed=50),
+    ms.LayerConfig("q8_hashscored_reduced_T9", 512, 32, 4, 256, 9, route="hash_scored", vocab=300, table_k=6,
+                   seed=51),
+    ms.LayerConfig("q8_hashscored_T70", 512, 64, 6, 256, 70, route="hash_scored", vocab=5000, seed=52),
+    ms.LayerConfig("q2_hash_reduced_T1", 512, 16, 4, 512, 1, routed_fmt="q2", route="hash", vocab=50, table_k=6,
+                   seed=53),
+    ms.LayerConfig("q8_hash_reduced_T40", 512, 32, 2, 256, 40, route="hash", vocab=400, table_k=6, seed=54),
+    ms.LayerConfig("e384_top8_T1", 512, 384, 8, 256, 1, seed=55),
+    ms.LayerConfig("e384_top8_T20", 512, 384, 8, 256, 20, seed=56),
+    ms.LayerConfig("e384_top8_T100", 512, 384, 8, 256, 100, seed=57),
 ]
 
 
@@ -241,7 +255,7 @@ def test_empty_batch_is_a_no_op():
 def test_batched_equals_single_token_calls_bitwise(cfg):
     inp, layer = case(cfg)
     x = torch.from_numpy(inp["x"]).cuda()
-    tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route == "hash" else None
+    tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route != "learned" else None
     full = layer.forward(x, tok).clone()
     again = layer.forward(x, tok).clone()
     assert torch.equal(full.view(torch.int32), again.view(torch.int32)), "two identical calls differ"
@@ -314,7 +328,8 @@ def test_check_hash_table():
 
 # ------------------------------------------------------ full-size layers
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["decode_q8", "decode_q2", "hash_decode"])
+@pytest.mark.parametrize("name", ["decode_q8", "decode_q2", "hash_decode", "decode_topk4", "hash_scored_decode",
+                                  "decode_motif3"])
 def test_full_size_decode(name):
     cfg = ms.CONFIGS[name]
     inp, layer = case(cfg)
@@ -348,7 +363,7 @@ def test_graph_replay_matches_eager(cfg):
     qr = _qr()
     inp, layer = case(cfg)
     x = torch.from_numpy(inp["x"]).cuda()
-    tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route == "hash" else None
+    tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route != "learned" else None
     want = layer.forward(x, tok).clone()
     out = torch.empty_like(want)
     layer.ensure_workspace(cfg.tokens)
