@@ -17,7 +17,7 @@
 // takes A[j][l%32] and B[j][l%32] with j = l/32 and puts product j in
 // registers [16j, 16j+16) with the same row/column mapping.
 //
-// Tile = 64 pairs x 64 columns.  K runs in chunks of 4 blocks staged in LDS
+// Tile = 64 pairs x 64 columns.  K runs in chunks of KC blocks staged in LDS
 // (padded rows), the next chunk's global loads held in registers meanwhile.
 // The scale products of two consecutive blocks come from one 2-block outer
 // product (lanes 0..31 supply block b, lanes 32..63 block b+1).
@@ -37,18 +37,23 @@ namespace qrmoe {
 
 constexpr int kTM = 64;                  // pairs per tile
 constexpr int kTN = 64;                  // columns per tile
-constexpr int kKC = 4;                   // blocks per staged K chunk
-constexpr int kRowB = kKC * 32 + 16;     // padded LDS row (bytes)
+// K chunk staged per step (KC blocks): gate/up 4 (its registers are full),
+// down 8 (twice the compute between a chunk's request and its use).
+constexpr int kKCGateUp = 4;
+constexpr int kKCDown = 8;
+template <int KC>
+constexpr int row_bytes() { return KC * 32 + 16; }  // padded LDS row (bytes)
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
-template <int NBR>
+template <int NBR, int KC>
 struct GemmSmem {
-    alignas(16) int8_t A[kTM][kRowB];    // activation codes of the chunk
-    alignas(16) int8_t B[NBR][kRowB];    // weight codes of the chunk
-    float sa[kKC][kTM];                  // activation block scales of the chunk
-    uint32_t sw[NBR][kKC / 2];           // weight block scales of the chunk (fp16 pairs)
+    static constexpr int kKC = KC;
+    alignas(16) int8_t A[kTM][row_bytes<KC>()];    // activation codes of the chunk
+    alignas(16) int8_t B[NBR][row_bytes<KC>()];    // weight codes of the chunk
+    float sa[KC][kTM];                             // activation block scales of the chunk
+    uint32_t sw[NBR][KC / 2];                      // weight block scales of the chunk (fp16 pairs)
     int32_t arow[kTM];                   // activation row of each tile row
     int32_t pair[kTM];
     float w[kTM];
@@ -60,44 +65,58 @@ __device__ __forceinline__ i32x4 g16nt(const void *p) {
 }
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-// Staging of one K chunk by NT threads: 16-byte activation and weight code
-// pieces, one activation block scale (threads < kKC * kTM) and one pair of
-// fp16 weight block scales (threads < 2 * NBR).  The global addresses of a
-// thread's pieces do not change from chunk to chunk and are set up once; the
-// compute phase reads only LDS, so no value loaded for a later chunk is
-// waited for early (a wave waits for its loads in issue order).
-template <int NT, int NBR>
+// Staging of one K chunk (kKC blocks) by NT threads: 16-byte activation and
+// weight code pieces, activation block scales and pairs of fp16 weight block
+// scales, spread evenly over the threads.  The global addresses of a thread's
+// pieces do not change from chunk to chunk and are set up once; the compute
+// phase reads only LDS, so no value loaded for a later chunk is waited for
+// early (a wave waits for its loads in issue order).
+template <int NT, int NBR, int kKC>
 struct Stage {
-    static constexpr int NA = kTM * 8 / NT;
-    static constexpr int NW = NBR * 8 / NT;
+    static constexpr int PR = kKC * 2;                   // 16-byte pieces per row and chunk
+    static constexpr int NA = kTM * PR / NT;
+    static constexpr int NW = NBR * PR / NT;
+    static constexpr int NS = (kKC * kTM + NT - 1) / NT;           // activation scales per thread
+    static constexpr int NWS = (NBR * (kKC / 2) + NT - 1) / NT;    // fp16 weight-scale pairs per thread
+    static_assert(NA >= 1 && NW >= 1 && kTM * PR % NT == 0 && NBR * PR % NT == 0, "staging geometry");
     const int8_t *pa[NA];
     const uint8_t *pb[NW];
-    const float *ps;
-    const uint32_t *pw;
+    const float *ps[NS];
+    const uint32_t *pw[NWS];
     i32x4 a[NA];
     i32x4 b[NW];
-    float s;
-    uint32_t w;
+    float s[NS];
+    uint32_t w[NWS];
 
     // bmat(j): weight matrix of B staging row j; brow0(j): its first row index
     template <int K, class BRow>
-    __device__ __forceinline__ void setup(const GemmSmem<NBR> &sm, const int8_t *__restrict__ act,
+    __device__ __forceinline__ void setup(const GemmSmem<NBR, kKC> &sm, const int8_t *__restrict__ act,
                                           const float *__restrict__ ascale, int64_t R, BRow brow) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            const int idx = tid + NT * i, row = idx / PR, piece = idx % PR;
             pa[i] = act + (int64_t)sm.arow[row] * K + piece * 16;
         }
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            const int idx = tid + NT * i, row = idx / PR, piece = idx % PR;
             pb[i] = brow(row).first + (int64_t)brow(row).second * K + piece * 16;
         }
-        const int m = tid & 63, kb = (tid >> 6) & (kKC - 1);
-        ps = ascale + (int64_t)sm.arow[m] * (K / 32) + kb;
-        const int wr = (tid >> 1) % NBR, wh = tid & 1;
-        pw = reinterpret_cast<const uint32_t *>(brow(wr).first + R * K) + ((int64_t)brow(wr).second * (K / 32)) / 2 + wh;
+        // (scale slots past the chunk's count point at slot 0 and load nothing)
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int idx = tid + NT * i < kKC * kTM ? tid + NT * i : 0;
+            const int m = idx & 63, kb = idx >> 6;
+            ps[i] = ascale + (int64_t)sm.arow[m] * (K / 32) + kb;
+        }
+#pragma unroll
+        for (int i = 0; i < NWS; ++i) {
+            const int idx = tid + NT * i < NBR * (kKC / 2) ? tid + NT * i : 0;
+            const int wr = idx / (kKC / 2), wh = idx % (kKC / 2);
+            pw[i] = reinterpret_cast<const uint32_t *>(brow(wr).first + R * K) +
+                    ((int64_t)brow(wr).second * (K / 32)) / 2 + wh;
+        }
     }
     __device__ __forceinline__ void load(int c) {
         const int tid = threadIdx.x;
@@ -105,29 +124,41 @@ struct Stage {
         for (int i = 0; i < NA; ++i) a[i] = g16(pa[i] + c * (kKC * 32));
 #pragma unroll
         for (int i = 0; i < NW; ++i) b[i] = g16nt(pb[i] + c * (kKC * 32));
-        if (tid < kKC * kTM) s = ps[c * kKC];
-        if (tid < 2 * NBR) w = pw[c * (kKC / 2)];
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            if (tid + NT * i < kKC * kTM) s[i] = ps[i][c * kKC];
+#pragma unroll
+        for (int i = 0; i < NWS; ++i)
+            if (tid + NT * i < NBR * (kKC / 2)) w[i] = pw[i][c * (kKC / 2)];
     }
-    __device__ __forceinline__ void store(GemmSmem<NBR> &sm) const {
+    __device__ __forceinline__ void store(GemmSmem<NBR, kKC> &sm) const {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            const int idx = tid + NT * i, row = idx / PR, piece = idx % PR;
             *reinterpret_cast<i32x4 *>(&sm.A[row][piece * 16]) = a[i];
         }
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int idx = tid + NT * i, row = idx >> 3, piece = idx & 7;
+            const int idx = tid + NT * i, row = idx / PR, piece = idx % PR;
             *reinterpret_cast<i32x4 *>(&sm.B[row][piece * 16]) = b[i];
         }
-        if (tid < kKC * kTM) sm.sa[tid >> 6][tid & 63] = s;
-        if (tid < 2 * NBR) sm.sw[tid >> 1][tid & 1] = w;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int idx = tid + NT * i;
+            if (idx < kKC * kTM) sm.sa[idx >> 6][idx & 63] = s[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NWS; ++i) {
+            const int idx = tid + NT * i;
+            if (idx < NBR * (kKC / 2)) sm.sw[idx / (kKC / 2)][idx % (kKC / 2)] = w[i];
+        }
     }
 };
 
 // Tile setup: pairs, activation rows (token for x, pair for h) and weights.
-template <int NBR>
-__device__ __forceinline__ void setup_tile(const LayerArgs &a, GemmSmem<NBR> &sm, int4 grp, bool shared,
+template <class Smem>
+__device__ __forceinline__ void setup_tile(const LayerArgs &a, Smem &sm, int4 grp, bool shared,
                                            bool act_is_h) {
     const int tid = threadIdx.x;
     const Dims &d = a.d;
@@ -142,8 +173,8 @@ __device__ __forceinline__ void setup_tile(const LayerArgs &a, GemmSmem<NBR> &sm
 }
 
 // fp16 weight scale of block kb (0..kKC-1) of staged weight row r
-template <int NBR>
-__device__ __forceinline__ float wscale(const GemmSmem<NBR> &sm, int r, int kb) {
+template <class Smem>
+__device__ __forceinline__ float wscale(const Smem &sm, int r, int kb) {
     const uint32_t v = sm.sw[r][kb >> 1];
     return f16_to_f32((uint16_t)((kb & 1) ? (v >> 16) : (v & 0xffff)));
 }
@@ -151,8 +182,9 @@ __device__ __forceinline__ float wscale(const GemmSmem<NBR> &sm, int r, int kb) 
 // ------------------------------------------------------------- gate / up
 template <int H, bool DUMP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gateup_mfma_kernel(LayerArgs a) {
-    constexpr int NT = 512, NB = H / 32, NC = NB / kKC, NBR = 2 * kTN;
-    __shared__ GemmSmem<NBR> sm;
+    constexpr int NT = 512, kKC = kKCGateUp, NB = H / 32, NC = NB / kKC, NBR = 2 * kTN;
+    static_assert(NC >= 1 && NB % kKC == 0, "K chunks");
+    __shared__ GemmSmem<NBR, kKC> sm;
     const int g = blockIdx.y;
     if (g >= a.ws.ctl[kCtlGroups]) return;
     const int4 grp = a.ws.groups[g];
@@ -172,7 +204,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    Stage<NT, NBR> st;
+    Stage<NT, NBR, kKC> st;
     st.template setup<H>(sm, a.ws.xq, a.ws.xd, d.F, brow);
     st.load(0);
 #pragma unroll 1
@@ -240,8 +272,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 // ------------------------------------------------------------------ down
 template <int F, bool DUMP>
 __global__ __launch_bounds__(256) void down_mfma_kernel(LayerArgs a) {
-    constexpr int NB = F / 32, NC = NB / kKC, NBR = kTN;
-    __shared__ GemmSmem<NBR> sm;
+    constexpr int kKC = kKCDown, NB = F / 32, NC = NB / kKC, NBR = kTN;
+    static_assert(NC >= 1 && NB % kKC == 0, "K chunks");
+    __shared__ GemmSmem<NBR, kKC> sm;
     const int g = blockIdx.y;
     if (g >= a.ws.ctl[kCtlGroups]) return;
     const int4 grp = a.ws.groups[g];
@@ -258,7 +291,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(LayerArgs a) {
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    Stage<256, NBR> st;
+    Stage<256, NBR, kKC> st;
     st.template setup<F>(sm, a.ws.hq, a.ws.hd, d.H, brow);
     st.load(0);
 #pragma unroll 1
