@@ -22,9 +22,15 @@
 namespace qrmoe {
 
 // ------------------------------------------------- sort + work-list build
-// Runs in ONE workgroup of 256 threads.  Stable counting sort of the P = T*k
-// pairs by expert; then the work list: each expert's pairs cut into groups of
-// at most G, followed by the shared expert's tokens cut the same way.
+// Stable counting sort of the P = T*k pairs by expert, then the work list:
+// each expert's pairs cut into groups of at most G, followed by the shared
+// expert's tokens cut the same way.  Up to kSortOneWg pairs it runs in ONE
+// workgroup of 256 threads; larger batches take three kernels: per-chunk
+// histograms, one workgroup for the prefix sums and the work list, and a
+// per-chunk stable scatter.
+constexpr int kSortOneWg = 4096;
+constexpr int kSortChunk = 1024;  // pairs per workgroup of the histogram and scatter kernels
+
 struct SortSmem {
     int cnt[1024];
     int off[1025];
@@ -36,47 +42,46 @@ struct SortSmem {
     int total;
 };
 
-__device__ void sort_and_group(const Dims &d, const Ws &ws, int G, SortSmem &sm) {
+// Stable placement of the pairs [base, base + 256) (this thread: base + tid)
+// given fill[e] = the next free slot of expert e in perm; advances fill.
+// Within the batch a pair's rank among the same expert's pairs comes from
+// the wave's ballots over the id bits, then the lower waves' counts.
+__device__ __forceinline__ void place_batch(const Ws &ws, int P, int base, int *fill, int (*wcnt)[1024]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = d.E, P = d.T * d.k;
-    for (int e = tid; e < E; e += 256) {
-        sm.cnt[e] = 0;
-        sm.fill[e] = 0;
-        for (int w = 0; w < 4; ++w) sm.wcnt[w][e] = 0;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int p = base + tid;
+    const bool valid = p < P;
+    const int e = valid ? ws.ids[p] : 1023 + 1;  // sentinel never matches a real expert
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 11; ++bit) {
+        const uint64_t b = __ballot((e >> bit) & 1);
+        same &= ((e >> bit) & 1) ? b : ~b;
+    }
+    const int rank_w = __popcll(same & lt_mask);
+    const bool leader = rank_w == 0;
+    if (valid && leader) wcnt[wave][e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+        int r = fill[e] + rank_w;
+        for (int w = 0; w < wave; ++w) r += wcnt[w][e];
+        ws.perm[r] = p;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += 256) atomicAdd(&sm.cnt[ws.ids[p]], 1);
+    if (valid && leader) {
+        atomicAdd(&fill[e], __popcll(same));
+        wcnt[wave][e] = 0;
+    }
     __syncthreads();
+}
+
+// counts, offsets and the work list from the per-expert counts in sm.cnt
+// (every thread of one workgroup)
+__device__ void write_work_list(const Dims &d, const Ws &ws, int G, SortSmem &sm) {
+    const int tid = threadIdx.x, E = d.E;
     block_excl_scan(sm.cnt, sm.off, E, sm.tmp, &sm.total);
     if (tid == 0) sm.off[E] = sm.total;
     __syncthreads();
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < P; base += 256) {
-        const int p = base + tid;
-        const bool valid = p < P;
-        const int e = valid ? ws.ids[p] : 1023 + 1;  // sentinel never matches a real expert
-        uint64_t same = ~0ull;
-#pragma unroll
-        for (int bit = 0; bit < 11; ++bit) {
-            const uint64_t b = __ballot((e >> bit) & 1);
-            same &= ((e >> bit) & 1) ? b : ~b;
-        }
-        const int rank_w = __popcll(same & lt_mask);
-        const bool leader = rank_w == 0;
-        if (valid && leader) sm.wcnt[wave][e] = __popcll(same);
-        __syncthreads();
-        if (valid) {
-            int r = sm.fill[e] + rank_w;
-            for (int w = 0; w < wave; ++w) r += sm.wcnt[w][e];
-            ws.perm[sm.off[e] + r] = p;
-        }
-        __syncthreads();
-        if (valid && leader) {
-            atomicAdd(&sm.fill[e], __popcll(same));
-            sm.wcnt[wave][e] = 0;
-        }
-        __syncthreads();
-    }
     for (int e = tid; e < E; e += 256) {
         ws.counts[e] = sm.cnt[e];
         ws.offsets[e] = sm.off[e];
@@ -97,6 +102,72 @@ __device__ void sort_and_group(const Dims &d, const Ws &ws, int G, SortSmem &sm)
     for (int j = tid; j < shared_groups; j += 256)
         ws.groups[routed_groups + j] = make_int4(E, j * G, min(G, d.T - j * G), 0);
     if (tid == 0) ws.ctl[kCtlGroups] = routed_groups + shared_groups;
+}
+
+__device__ void sort_and_group(const Dims &d, const Ws &ws, int G, SortSmem &sm) {
+    const int tid = threadIdx.x;
+    const int E = d.E, P = d.T * d.k;
+    for (int e = tid; e < E; e += 256) {
+        sm.cnt[e] = 0;
+        for (int w = 0; w < 4; ++w) sm.wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += 256) atomicAdd(&sm.cnt[ws.ids[p]], 1);
+    __syncthreads();
+    write_work_list(d, ws, G, sm);
+    for (int e = tid; e < E; e += 256) sm.fill[e] = sm.off[e];
+    __syncthreads();
+    for (int base = 0; base < P; base += 256) place_batch(ws, P, base, sm.fill, sm.wcnt);
+}
+
+// Per-chunk expert histograms hist[chunk][e], kept in the y region of the
+// workspace (unused until the down projection writes it).
+__device__ __forceinline__ int *sort_hist(const Ws &ws) { return reinterpret_cast<int *>(ws.y); }
+
+__global__ __launch_bounds__(256) void sort_hist_kernel(LayerArgs a) {
+    __shared__ int cnt[1024];
+    const int tid = threadIdx.x, c = blockIdx.x, E = a.d.E, P = a.d.T * a.d.k;
+    for (int e = tid; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    const int end = min(P, (c + 1) * kSortChunk);
+    for (int p = c * kSortChunk + tid; p < end; p += 256) atomicAdd(&cnt[a.ws.ids[p]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) sort_hist(a.ws)[(int64_t)c * E + e] = cnt[e];
+}
+
+// One workgroup: hist[c][e] becomes the number of expert-e pairs in chunks
+// before c; the totals give counts, offsets and the work list.
+__global__ __launch_bounds__(256) void sort_scan_kernel(LayerArgs a, int nchunks) {
+    __shared__ SortSmem sm;
+    const int tid = threadIdx.x, E = a.d.E;
+    int *hist = sort_hist(a.ws);
+    for (int e = tid; e < E; e += 256) {
+        int run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int v = hist[(int64_t)c * E + e];
+            hist[(int64_t)c * E + e] = run;
+            run += v;
+        }
+        sm.cnt[e] = run;
+    }
+    __syncthreads();
+    write_work_list(a.d, a.ws, a.group_tok, sm);
+}
+
+// Per chunk: each pair's slot = offset of its expert + that expert's pairs in
+// earlier chunks + its rank within the chunk (stable).
+__global__ __launch_bounds__(256) void sort_scatter_kernel(LayerArgs a) {
+    __shared__ int fill[1024];
+    __shared__ int wcnt[4][1024];
+    const int tid = threadIdx.x, c = blockIdx.x, E = a.d.E, P = a.d.T * a.d.k;
+    const int *hist = sort_hist(a.ws);
+    for (int e = tid; e < E; e += 256) {
+        fill[e] = a.ws.offsets[e] + hist[(int64_t)c * E + e];
+        for (int w = 0; w < 4; ++w) wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    const int end = min(P, (c + 1) * kSortChunk);
+    for (int base = c * kSortChunk; base < end; base += 256) place_batch(a.ws, end, base, fill, wcnt);
 }
 
 // --------------------------------------------------- batched (large T)
@@ -305,7 +376,16 @@ __global__ __launch_bounds__(256) void sort_kernel(LayerArgs a) {
 }
 
 hipError_t launch_sort(const LayerArgs &a, hipStream_t s) {
-    klaunch(sort_kernel, dim3(1), dim3(256), s, a);
+    const int P = a.d.T * a.d.k;
+    if (P <= kSortOneWg) {
+        klaunch(sort_kernel, dim3(1), dim3(256), s, a);
+        return hipGetLastError();
+    }
+    // the histograms (nchunks * E ints) fit the y region (P * H floats) by far
+    const int nchunks = (P + kSortChunk - 1) / kSortChunk;
+    klaunch(sort_hist_kernel, dim3(nchunks), dim3(256), s, a);
+    klaunch(sort_scan_kernel, dim3(1), dim3(256), s, a, nchunks);
+    klaunch(sort_scatter_kernel, dim3(nchunks), dim3(256), s, a);
     return hipGetLastError();
 }
 

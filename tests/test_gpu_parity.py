@@ -209,6 +209,23 @@ def test_skewed_bias_mfma_tiles():
     check(cfg, inp, g, stride=4, name="skew_mfma")
 
 
+@pytest.mark.parametrize("skew", [False, True])
+def test_chunked_sort_ragged_and_skewed(skew):
+    """4400 pairs: the sort runs as per-chunk histograms, one prefix workgroup and
+    a per-chunk stable scatter (five 1024-pair chunks, the last one ragged);
+    with a bias that gives one expert every token, that expert's pairs span
+    every chunk."""
+    cfg = ms.LayerConfig("sort_chunks_skew" if skew else "sort_chunks", 256, 64, 4, 256, 1100, seed=60 + skew)
+    inp = ms.make_inputs(cfg)
+    if skew:
+        inp["router_b"][9] = 10.0
+    layer = _qr().MoELayer(256, 64, 4, 256).load(inp)
+    g = run_gpu(cfg, inp, layer, stride=8)
+    if skew:
+        assert g["counts"][9] == 1100
+    check(cfg, inp, g, rows=np.r_[0:6, 500:506, 1094:1100], stride=8, name=cfg.name)
+
+
 @pytest.mark.parametrize("T", [1, 7, 40])
 def test_tied_keys_take_the_smaller_expert_ids(T):
     """Experts share router rows and biases in groups of four, so every
