@@ -209,9 +209,18 @@ struct Sel1Smem {
     int32_t flags;     // hash-path flags of workgroups other than (0, 0)
 };
 
-constexpr int kG1Rows = 64;   // rows of one workgroup: two h blocks
+constexpr int kG1Rows = 64;   // rows of a routed workgroup: two h blocks
+// Rows of a shared-expert workgroup: one h block where a wave pass allows it,
+// so the shared expert's rows spread over twice as many workgroups (one slot
+// per 32 rows of each 64-row column); the shared expert is Q8 even when the
+// routed experts are 2-bit, and with one slot its workgroups would stream
+// three times the bytes of a 2-bit routed one.
 constexpr int kMaxSelList = 9;  // work-list entries the one-token down kernel reads (top_k <= 8, shared)
 constexpr int kG1Waves = 8;
+template <int K>
+constexpr int g1_shared_rows() {
+    return kG1Waves * Geo<K, kFmtQ8>::RPW > 32 ? kG1Waves * Geo<K, kFmtQ8>::RPW : 32;
+}
 
 template <int K, int FMT, bool DUMP>
 __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
@@ -220,13 +229,14 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int slot = blockIdx.y;
-    if (slot == d.k) {  // shared expert (pair k): needs no routing, streams while the others select
+    if (slot >= d.k) {  // shared expert (pair k): needs no routing, streams while the others select
+        constexpr int SR = g1_shared_rows<K>();
         if (tid == 0) {
             sm.pair[0] = d.k;
             sm.row[0] = 0;
         }
-        gateup_rows<K, kFmtQ8, kVecTok, kG1Rows, true, DUMP, kG1Waves>(
-            a, sm, a.wt.sh_gate, a.wt.sh_up, 1, blockIdx.x * kG1Rows, [&] {
+        gateup_rows<K, kFmtQ8, kVecTok, SR, true, DUMP, kG1Waves>(
+            a, sm, a.wt.sh_gate, a.wt.sh_up, 1, ((slot - d.k) * gridDim.x + blockIdx.x) * SR, [&] {
                 for (int i = tid; i < K / 16; i += 64 * kG1Waves) {
                     reinterpret_cast<int4 *>(sm.aq[0])[i] = reinterpret_cast<const int4 *>(a.ws.xq)[i];
                     if (i < K / 32) sm.ad[0][i] = a.ws.xd[i];
@@ -490,16 +500,22 @@ hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// grid: (F / 64 columns) x (k routed slots + the shared expert's slots)
+template <int K, int FMT, bool DUMP>
+static void gateup1_launch(const LayerArgs &a, hipStream_t s) {
+    const int nsh = a.d.has_shared ? kG1Rows / g1_shared_rows<K>() : 0;
+    klaunch(decode_gateup1_kernel<K, FMT, DUMP>, dim3(a.d.F / kG1Rows, a.d.k + nsh), dim3(64 * kG1Waves), s, a);
+}
+
 template <int FMT, bool DUMP>
 static hipError_t gateup1_f(const LayerArgs &a, hipStream_t s) {
-    const dim3 grid(a.d.F / kG1Rows, a.d.k + a.d.has_shared), block(64 * kG1Waves);
     switch (a.d.H) {
-        case 128: if constexpr (FMT == kFmtQ8) { klaunch(decode_gateup1_kernel<128, FMT, DUMP>, grid, block, s, a); break; } return hipErrorInvalidValue;
-        case 256: if constexpr (FMT == kFmtQ8) { klaunch(decode_gateup1_kernel<256, FMT, DUMP>, grid, block, s, a); break; } return hipErrorInvalidValue;
-        case 512: klaunch(decode_gateup1_kernel<512, FMT, DUMP>, grid, block, s, a); break;
-        case 1024: klaunch(decode_gateup1_kernel<1024, FMT, DUMP>, grid, block, s, a); break;
-        case 2048: klaunch(decode_gateup1_kernel<2048, FMT, DUMP>, grid, block, s, a); break;
-        case 4096: klaunch(decode_gateup1_kernel<4096, FMT, DUMP>, grid, block, s, a); break;
+        case 128: if constexpr (FMT == kFmtQ8) { gateup1_launch<128, FMT, DUMP>(a, s); break; } return hipErrorInvalidValue;
+        case 256: if constexpr (FMT == kFmtQ8) { gateup1_launch<256, FMT, DUMP>(a, s); break; } return hipErrorInvalidValue;
+        case 512: gateup1_launch<512, FMT, DUMP>(a, s); break;
+        case 1024: gateup1_launch<1024, FMT, DUMP>(a, s); break;
+        case 2048: gateup1_launch<2048, FMT, DUMP>(a, s); break;
+        case 4096: gateup1_launch<4096, FMT, DUMP>(a, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

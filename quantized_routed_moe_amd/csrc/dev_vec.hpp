@@ -184,45 +184,54 @@ struct GuRows {
     static constexpr int v = 4 * Geo<K, FMT>::RPW > 8 ? 4 * Geo<K, FMT>::RPW : 8;
 };
 
+// Ring depth of gate/up rows (row passes held by a wave): the current pass
+// and the next two in flight.  (Six for the small 2-bit rows measured
+// slower: the one-token 2-bit gate/up is not bound by rows in flight.)
+template <int K, int FMT>
+struct GuDepth {
+    static constexpr int v = 3;
+};
+
 // Gate/up of one expert for rows r0..r0+ROWS-1 and the cnt staged tokens,
 // then SwiGLU.  QUANT: quantize the 32-row h block of every token here
 // (ROWS == 32) into hq/hd; otherwise store h in fp32 for the consumer to
 // quantize (the same values give the same codes wherever they are
 // quantized).  sm.pair[] names the output pair of each token.
 //
-// Each wave keeps the rows of the next two passes in flight.  The first two
-// are requested before `stage()` runs (the caller's activation staging, which
-// ends with a barrier), so weight streaming starts as soon as the expert is
-// known.
-// NW waves per workgroup; with QUANT the workgroup's NW*64 threads cover
-// NTOK tokens x ROWS rows of h (ROWS a multiple of the 32-row h block).
+// Each wave keeps the rows of the next DEPTH - 1 passes in flight (a ring of
+// DEPTH gate and up rows, indexed at compile time).  The first DEPTH - 1 are
+// requested before `stage()` (the caller's activation staging, which ends
+// with a barrier), so weight streaming starts as soon as the expert is known.
+// NW waves per workgroup; with QUANT the workgroup's NW*64 threads cover (at
+// least) NTOK tokens x ROWS rows of h (ROWS a multiple of the 32-row h block).
 template <int K, int FMT, int NTOK, int ROWS, bool QUANT, bool DUMP, int NW = 4, class Stage>
 __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint8_t *__restrict__ gmat,
                             const uint8_t *__restrict__ umat, int cnt, int r0, Stage stage) {
     using G = Geo<K, FMT>;
     using RR = RowRegs<K, FMT, G::L>;
     constexpr int PASSES = ROWS / (NW * G::RPW);
+    constexpr int DEPTH = GuDepth<K, FMT>::v < PASSES + 1 ? GuDepth<K, FMT>::v : PASSES + 1;
     static_assert(PASSES >= 1 && ROWS % (NW * G::RPW) == 0, "row geometry");
-    static_assert(!QUANT || (ROWS % kVecRows == 0 && ROWS <= 2 * kVecRows && NW * 64 == NTOK * ROWS), "h blocks");
+    static_assert(!QUANT || (ROWS % kVecRows == 0 && ROWS <= 2 * kVecRows && NW * 64 >= NTOK * ROWS), "h blocks");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int seg = lane % G::L, rsub = lane / G::L;
     auto row_of = [&](int pass) { return (pass * NW + wave) * G::RPW + rsub; };
-    RR wg0, wu0, wg1, wu1;
-    wg0.load(gmat, d.F, r0 + row_of(0), seg);
-    wu0.load(umat, d.F, r0 + row_of(0), seg);
-    if (PASSES > 1) {
-        wg1.load(gmat, d.F, r0 + row_of(1), seg);
-        wu1.load(umat, d.F, r0 + row_of(1), seg);
-    }
+    RR wg[DEPTH], wu[DEPTH];
+#pragma unroll
+    for (int q = 0; q < DEPTH - 1; ++q)
+        if (q < PASSES) {
+            wg[q].load(gmat, d.F, r0 + row_of(q), seg);
+            wu[q].load(umat, d.F, r0 + row_of(q), seg);
+        }
     stage();
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-        RR ng, nu;
-        if (pass + 2 < PASSES) {
-            ng.load(gmat, d.F, r0 + row_of(pass + 2), seg);
-            nu.load(umat, d.F, r0 + row_of(pass + 2), seg);
+        if (pass + DEPTH - 1 < PASSES) {
+            wg[(pass + DEPTH - 1) % DEPTH].load(gmat, d.F, r0 + row_of(pass + DEPTH - 1), seg);
+            wu[(pass + DEPTH - 1) % DEPTH].load(umat, d.F, r0 + row_of(pass + DEPTH - 1), seg);
         }
+        const RR &g0 = wg[pass % DEPTH], &u0 = wu[pass % DEPTH];
         const int row_local = row_of(pass);
         const int r = r0 + row_local;
         const bool dump_row = DUMP && (r % a.dump.stride == 0);
@@ -234,8 +243,8 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
                 dg = a.dump.gate_sums + base;
                 du = a.dump.up_sums + base;
             }
-            const float gp = group_sum<G::L>(lane_dot<K, G::L>(wg0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dg));
-            const float up = group_sum<G::L>(lane_dot<K, G::L>(wu0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, du));
+            const float gp = group_sum<G::L>(lane_dot<K, G::L>(g0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dg));
+            const float up = group_sum<G::L>(lane_dot<K, G::L>(u0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, du));
             if (seg == 0) {
                 const float hv = swiglu(gp, up);
                 if constexpr (QUANT)
@@ -244,14 +253,10 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
                     a.ws.h[(int64_t)sm.pair[tok] * d.F + r] = hv;
             }
         }
-        wg0 = wg1;
-        wu0 = wu1;
-        wg1 = ng;
-        wu1 = nu;
     }
     if constexpr (QUANT) {
         __syncthreads();
-        const int tok = tid / ROWS, i = tid % ROWS;  // 32 consecutive lanes = one h block of one token
+        const int tok = tid / ROWS, i = tid % ROWS;  // 32 consecutive lanes = one h block of one token (tok < NTOK...)
         const float v = tok < cnt ? sm.h[tok][i] : 0.0f;
         const float amax = group_max<32>(fabsf(v));
         if (tok < cnt) {
