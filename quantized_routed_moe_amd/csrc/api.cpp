@@ -221,7 +221,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
             run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
         }
     } else {
-        // Q8 experts go through the grouped int8 MFMA GEMMs (32-pair tiles);
+        // Q8 experts go through the grouped int8 MFMA GEMMs (64-pair tiles);
         // 2-bit experts and the smallest shapes stay on the VALU kernels.
         const bool mfma = shape->routed_fmt == MOE_FMT_Q8_32 && H >= 256 && shape->ffn >= 256;
         const int64_t tiles = mfma ? max_groups(shape, T, kMfmaTile) : mg;
