@@ -29,6 +29,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (TOP/s)
+# fp32 vector ALU issue rate without packed dual-issue: 256 CUs x 4 SIMDs x 16
+# lanes x 2.4 GHz single-lane operations per second (the 157.3 TFLOP/s vector
+# peak counts an FMA as 2 flops and packed fp32 as 2 lanes; this code issues
+# neither packed fp32 nor anything wider)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill)"
 
 
@@ -127,7 +132,9 @@ def stage_model(cfg, qr, u_avg):
     expert that receives a token, router weights, activations read and
     results written (x fp32, int8 codes + fp32 block scales, fp32 h, fp32
     y, fp32 out).  u_avg is the mean number of distinct routed experts per
-    step.  Ops count 2 per int8 multiply-add of the expert GEMMs."""
+    step.  Ops count 2 per int8 multiply-add of the expert GEMMs; valu counts
+    the per-block dequantization the Q8_32 format requires of them, one
+    int32 -> fp32 conversion and one fma per output and 32-block."""
     T, H, E, k, F = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn
     fmt = qr.FMT[cfg.routed_fmt]
     sh = 1 if cfg.shared else 0
@@ -167,8 +174,10 @@ def stage_model(cfg, qr, u_avg):
         st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + P * H * 4
         st["combine"] = P * H * 4 + x32
     ops = {"gateup": 2 * P * 2 * F * H, "down": 2 * P * H * F}
+    valu = {"gateup": 2 * P * 2 * F * (H // 32), "down": 2 * P * H * (F // 32)}
     layer = (u_avg * (2 * mr_gu + mr_dn) + sh * (2 * mq8_gu + mq8_dn) + (E * H * 4 if has_router else 0) + 2 * x32)
-    return {"stages": {s: {"bytes": b, "ops": ops.get(s)} for s, b in st.items()}, "layer_bytes": layer}
+    return {"stages": {s: {"bytes": b, "ops": ops.get(s), "valu": valu.get(s)} for s, b in st.items()},
+            "layer_bytes": layer}
 
 
 def stored_traffic(cfg, kernel):
@@ -190,26 +199,37 @@ def stored_traffic(cfg, kernel):
 
 def make_roofline(cfg, model, dom, dom_us):
     """Roofline entry of the dominant stage's kernel.  An MFMA GEMM is priced
-    against the roof that binds it at this workload: its weight bytes at the
-    HBM peak or its int8 operations at the MFMA peak, whichever takes longer
-    (at a few dozen tokens per expert the weights dominate and the roof is
-    HBM); the other roof's fraction is reported beside it."""
+    against the roof that binds it at this workload, the one its algorithmic
+    work takes longest on at peak: weight bytes over HBM, int8 operations
+    over the MFMA units, or the per-block dequantization (conversion + fma
+    per output and block) over the vector ALUs; the other roofs' fractions
+    are reported beside it."""
     kern = stage_kernel(cfg, dom)
     st = model["stages"].get(dom, {})
     traffic = stored_traffic(cfg, kern)
-    b, ops = st.get("bytes"), st.get("ops")
+    b, ops, valu = st.get("bytes"), st.get("ops"), st.get("valu")
     base = {"traffic": traffic, "kernel": kern, "stage": dom, "avg_launch_us": round(dom_us, 3),
             "algorithmic_bytes_per_launch": int(b) if b else None}
-    gbs = b / (dom_us * 1e-6) / 1e9 if b else None
-    if kern in ("gateup_mfma_kernel", "down_mfma_kernel"):
-        tops = ops / (dom_us * 1e-6) / 1e12
-        base["algorithmic_ops_per_launch"] = int(ops)
-        if ops / (INT8_PEAK_TOPS * 1e12) > b / (HBM_PEAK_GBS * 1e9):   # seconds at each peak
-            return {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                    "frac": round(tops / INT8_PEAK_TOPS, 4), **base, "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        base["mfma_frac"] = round(tops / INT8_PEAK_TOPS, 4)
-    return {"bound": "hbm", "achieved": round(gbs, 1) if b else None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4) if b else None, **base}
+    sec = dom_us * 1e-6
+    hbm = {"bound": "hbm", "achieved": round(b / sec / 1e9, 1) if b else None, "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(b / sec / 1e9 / HBM_PEAK_GBS, 4) if b else None}
+    if kern not in ("gateup_mfma_kernel", "down_mfma_kernel"):
+        return {**hbm, **base}
+    roofs = {
+        "hbm": (b / (HBM_PEAK_GBS * 1e9), hbm),
+        "mfma": (ops / (INT8_PEAK_TOPS * 1e12),
+                 {"bound": "mfma", "achieved": round(ops / sec / 1e12, 1), "peak": INT8_PEAK_TOPS,
+                  "unit": "TOP/s", "frac": round(ops / sec / 1e12 / INT8_PEAK_TOPS, 4)}),
+        "alu": (valu / (VALU_PEAK_TOPS * 1e12),
+                {"bound": "alu", "achieved": round(valu / sec / 1e12, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                 "unit": "T VALU lane-op/s", "frac": round(valu / sec / 1e12 / VALU_PEAK_TOPS, 4)}),
+    }
+    bind = max(roofs, key=lambda r: roofs[r][0])
+    out = {**roofs[bind][1], **base, "algorithmic_ops_per_launch": int(ops), "algorithmic_valu_per_launch": int(valu)}
+    for r, (_, e) in roofs.items():
+        if r != bind:
+            out[f"{r}_frac"] = e["frac"]
+    return out
 
 
 def traffic_from(args):
