@@ -209,20 +209,25 @@ struct Sel1Smem {
     int32_t flags;     // hash-path flags of workgroups other than (0, 0)
 };
 
-constexpr int kG1Rows = 64;   // rows of a routed workgroup: two h blocks
+// Two workgroup shapes: 64 rows (two h blocks) x 8 waves while the grid
+// holds at most one workgroup per CU, else 32 rows (one h block) x 4 waves,
+// whose smaller workgroups share CUs (at top-8 of 384 experts the wide grid
+// needs a second round).
+constexpr int kG1Rows = 64, kG1Waves = 8;
+constexpr int kG1RowsNarrow = 32, kG1WavesNarrow = 4;
+constexpr int kG1OneRound = 256;  // workgroups of one round of the wide shape (one per CU)
 // Rows of a shared-expert workgroup: one h block where a wave pass allows it,
-// so the shared expert's rows spread over twice as many workgroups (one slot
-// per 32 rows of each 64-row column); the shared expert is Q8 even when the
-// routed experts are 2-bit, and with one slot its workgroups would stream
-// three times the bytes of a 2-bit routed one.
+// so the shared expert's rows spread over more workgroups (one slot per 32
+// rows of each column); the shared expert is Q8 even when the routed experts
+// are 2-bit, and with one slot its workgroups would stream three times the
+// bytes of a 2-bit routed one.
 constexpr int kMaxSelList = 9;  // work-list entries the one-token down kernel reads (top_k <= 8, shared)
-constexpr int kG1Waves = 8;
-template <int K>
+template <int K, int NW>
 constexpr int g1_shared_rows() {
-    return kG1Waves * Geo<K, kFmtQ8>::RPW > 32 ? kG1Waves * Geo<K, kFmtQ8>::RPW : 32;
+    return NW * Geo<K, kFmtQ8>::RPW > 32 ? NW * Geo<K, kFmtQ8>::RPW : 32;
 }
 
-template <int K, int FMT, bool DUMP>
+template <int K, int FMT, bool DUMP, int ROWS, int NW>
 __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
     __shared__ VecSmem<K, kVecTok> sm;
     __shared__ Sel1Smem ss;
@@ -230,14 +235,14 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
     const Dims &d = a.d;
     const int slot = blockIdx.y;
     if (slot >= d.k) {  // shared expert (pair k): needs no routing, streams while the others select
-        constexpr int SR = g1_shared_rows<K>();
+        constexpr int SR = g1_shared_rows<K, NW>();
         if (tid == 0) {
             sm.pair[0] = d.k;
             sm.row[0] = 0;
         }
-        gateup_rows<K, kFmtQ8, kVecTok, SR, true, DUMP, kG1Waves>(
+        gateup_rows<K, kFmtQ8, kVecTok, SR, true, DUMP, NW>(
             a, sm, a.wt.sh_gate, a.wt.sh_up, 1, ((slot - d.k) * gridDim.x + blockIdx.x) * SR, [&] {
-                for (int i = tid; i < K / 16; i += 64 * kG1Waves) {
+                for (int i = tid; i < K / 16; i += 64 * NW) {
                     reinterpret_cast<int4 *>(sm.aq[0])[i] = reinterpret_cast<const int4 *>(a.ws.xq)[i];
                     if (i < K / 32) sm.ad[0][i] = a.ws.xd[i];
                 }
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
         if (lane == 0) ss.nuniq = __popcll(firsts);
     } else {
         // meanwhile the token's quantized x goes to LDS slot 0
-        for (int i = tid - 64; i < K / 16; i += 64 * (kG1Waves - 1)) {
+        for (int i = tid - 64; i < K / 16; i += 64 * (NW - 1)) {
             reinterpret_cast<int4 *>(sm.aq[0])[i] = reinterpret_cast<const int4 *>(a.ws.xq)[i];
             if (i < K / 32) sm.ad[0][i] = a.ws.xd[i];
             if (FMT == kFmtQ2) sm.as16[0][i] = a.ws.xs16[i];
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
             a.ws.w[tid] = ss.w[tid];
             a.ws.perm[tid] = ss.pairs[tid];
         }
-        for (int e = tid; e < d.E; e += 64 * kG1Waves) {
+        for (int e = tid; e < d.E; e += 64 * NW) {
             int c = 0, below = 0;
             for (int i = 0; i < k; ++i) {
                 c += ss.ids[i] == e;
@@ -331,15 +336,15 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
         sm.row[tid] = 0;
     }
     // a repeated expert (cnt > 1) applies to the same x: copy slot 0
-    for (int i = tid; i < (cnt - 1) * (K / 16); i += 64 * kG1Waves) {
+    for (int i = tid; i < (cnt - 1) * (K / 16); i += 64 * NW) {
         const int tok = 1 + i / (K / 16), c = i % (K / 16);
         reinterpret_cast<int4 *>(sm.aq[tok])[c] = reinterpret_cast<const int4 *>(sm.aq[0])[c];
         if (c < K / 32) sm.ad[tok][c] = sm.ad[0][c];
         if (FMT == kFmtQ2) sm.as16[tok][c] = sm.as16[0][c];
     }
     const int64_t mb = mat_bytes(FMT, d.F, K);
-    gateup_rows<K, FMT, kVecTok, kG1Rows, true, DUMP, kG1Waves>(a, sm, a.wt.gate + e * mb, a.wt.up + e * mb, cnt,
-                                                               blockIdx.x * kG1Rows, [&] { __syncthreads(); });
+    gateup_rows<K, FMT, kVecTok, ROWS, true, DUMP, NW>(a, sm, a.wt.gate + e * mb, a.wt.up + e * mb, cnt,
+                                                               blockIdx.x * ROWS, [&] { __syncthreads(); });
 }
 
 // -------------------------------------------------------- down, one token
@@ -500,11 +505,20 @@ hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// grid: (F / 64 columns) x (k routed slots + the shared expert's slots)
+// grid: (F / ROWS columns) x (k routed slots + the shared expert's slots)
+template <int K, int FMT, bool DUMP, int ROWS, int NW>
+static void gateup1_grid(const LayerArgs &a, hipStream_t s) {
+    const int nsh = a.d.has_shared ? ROWS / g1_shared_rows<K, NW>() : 0;
+    klaunch(decode_gateup1_kernel<K, FMT, DUMP, ROWS, NW>, dim3(a.d.F / ROWS, a.d.k + nsh), dim3(64 * NW), s, a);
+}
+
 template <int K, int FMT, bool DUMP>
 static void gateup1_launch(const LayerArgs &a, hipStream_t s) {
-    const int nsh = a.d.has_shared ? kG1Rows / g1_shared_rows<K>() : 0;
-    klaunch(decode_gateup1_kernel<K, FMT, DUMP>, dim3(a.d.F / kG1Rows, a.d.k + nsh), dim3(64 * kG1Waves), s, a);
+    const int nsh = a.d.has_shared ? kG1Rows / g1_shared_rows<K, kG1Waves>() : 0;
+    if ((a.d.F / kG1Rows) * (a.d.k + nsh) <= kG1OneRound)
+        gateup1_grid<K, FMT, DUMP, kG1Rows, kG1Waves>(a, s);
+    else
+        gateup1_grid<K, FMT, DUMP, kG1RowsNarrow, kG1WavesNarrow>(a, s);
 }
 
 template <int FMT, bool DUMP>

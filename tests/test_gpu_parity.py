@@ -169,6 +169,10 @@ SMALL = [
     ms.LayerConfig("e384_top8_T1", 512, 384, 8, 256, 1, seed=55),
     ms.LayerConfig("e384_top8_T20", 512, 384, 8, 256, 20, seed=56),
     ms.LayerConfig("e384_top8_T100", 512, 384, 8, 256, 100, seed=57),
+    # one token with more gate/up workgroups than CUs in the 64-row shape: the 32-row shape runs
+    ms.LayerConfig("q8_narrow_T1", 512, 32, 4, 4096, 1, seed=58),
+    ms.LayerConfig("q2_narrow_T1", 512, 16, 6, 4096, 1, routed_fmt="q2", seed=59),
+    ms.LayerConfig("q8_hash_narrow_T1", 512, 16, 6, 4096, 1, route="hash", vocab=7, seed=62),
 ]
 
 
