@@ -5,9 +5,9 @@
 //          sum a quarter of the adjacent-pair tree); for 2..32 tokens further
 //          workgroups stream the shared expert's gate/up rows, which need no
 //          routing, leaving its h in fp32.
-//  select  one workgroup: top-k or hash selection, sort, work list, and the
-//          quantization of the shared expert's h.
-//  gateup  routed experts' gate/up + SwiGLU + h quantization (expert_vec.hip).
+//  select  one workgroup: top-k or hash selection, sort, work list.
+//  gateup  routed experts' gate/up + SwiGLU + h quantization, and the
+//          quantization of the shared expert's h (expert_vec.hip).
 //  down    T == 1: one kernel computes every output row from all selected
 //          experts at once (each wave holds the row of every expert in
 //          registers, requested before anything else) and sums w * y in
@@ -92,12 +92,11 @@ __global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_le
 // ----------------------------------------------------------------- select
 // One workgroup: top-k (or hash lookup) of every token, stable sort of the
 // P = T*k <= 256 pairs by expert (rank = number of pairs with a smaller
-// expert, or the same expert and a smaller pair index), the work list
+// expert, or the same expert and a smaller pair index), and the work list
 // (each expert's pairs cut into runs of at most kVecTok, experts ascending,
-// then the shared expert's token runs), and the quantization of the shared
-// expert's h, which the front kernel left in fp32.
+// then the shared expert's token runs).
 struct SelectSmem {
-    int32_t ids[kDecodeMaxT * 8];
+    alignas(16) int32_t ids[kDecodeMaxT * 8];  // padded to a multiple of 4 with INT_MAX (counted nowhere)
     float w[kDecodeMaxT * 8];
     int32_t perm[kDecodeMaxT * 8];
     int32_t gpos[kDecodeMaxT * 8 + 1];
@@ -105,41 +104,70 @@ struct SelectSmem {
     int32_t ngroups;
 };
 
+// Learned routing, one token per wave at a time: the wave's next token's keys
+// and scores are requested before the current token is selected.
+template <int PER>
+__device__ void select_learned_tokens(const LayerArgs &a, SelectSmem &rs, int wave, int lane) {
+    const Dims &d = a.d;
+    KeyRegs<PER> cur;
+    if (wave < d.T) cur.load(a.ws.keys + (int64_t)wave * d.E, a.ws.scores + (int64_t)wave * d.E, d.E, lane);
+    for (int t = wave; t < d.T; t += 4) {
+        KeyRegs<PER> nxt;
+        if (t + 4 < d.T) nxt.load(a.ws.keys + (int64_t)(t + 4) * d.E, a.ws.scores + (int64_t)(t + 4) * d.E, d.E, lane);
+        int id;
+        float w;
+        select_keys_from<PER>(cur, d.k, id, w, lane);
+        if (lane < d.k) {
+            rs.ids[t * d.k + lane] = id;
+            rs.w[t * d.k + lane] = w;
+        }
+        cur = nxt;
+    }
+}
+
 __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
     __shared__ SelectSmem rs;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int P = d.T * d.k;
-    // waves 1..3 quantize the shared expert's h (independent of the routing)
-    // while wave 0 starts on the selection; for T > 1 all waves select
-    if (d.has_shared && wave > 0) {
-        const int nb = d.T * (d.F / 32);
-        const float *__restrict__ hsrc = a.ws.h;
-        int8_t *__restrict__ hq = a.ws.hq;
-        float *__restrict__ hd = a.ws.hd;
-#pragma unroll 4
-        for (int i = tid - 64; i < nb; i += 192) {
-            const int64_t p = (int64_t)d.T * d.k + i / (d.F / 32);
-            const int b = i % (d.F / 32);
-            quant_one_block(hsrc + p * d.F, hq + p * d.F, hd + p * (d.F / 32), nullptr, b);
+    // (the shared expert's h, fp32 from the front kernel, is quantized by the
+    // gate/up kernel's otherwise idle shared-group workgroups)
+    if (d.route == kRouteLearned) {
+        if (d.E <= 64) select_learned_tokens<1>(a, rs, wave, lane);
+        else if (d.E <= 128) select_learned_tokens<2>(a, rs, wave, lane);
+        else if (d.E <= 256) select_learned_tokens<4>(a, rs, wave, lane);
+        else if (d.E <= 512) select_learned_tokens<8>(a, rs, wave, lane);
+        else select_learned_tokens<16>(a, rs, wave, lane);
+    } else {
+        // eight lanes per token: the workgroup routes 32 tokens per pass
+        for (int t0 = 0; t0 < d.T; t0 += 32) {
+            const int t = t0 + wave * 8 + lane / 8, j = lane & 7;
+            const bool valid = t < d.T;
+            int id;
+            float w;
+            select_hash_group8(a.token_ids, a.wt.table, valid ? t : 0, valid, d.vocab, d.table_k, d.E, d.k, id, w,
+                               a.ws.ctl + kCtlFlags, d.route == kRouteHashScored ? a.ws.scores : nullptr, lane);
+            if (valid && j < d.k) {
+                rs.ids[t * d.k + j] = id;
+                rs.w[t * d.k + j] = w;
+            }
         }
     }
-    for (int t = wave; t < d.T; t += 4) {
-        if (d.route == kRouteLearned)
-            select_keys_wave(a.ws.keys + (int64_t)t * d.E, a.ws.scores + (int64_t)t * d.E, d.E, d.k, rs.ids + t * d.k,
-                             rs.w + t * d.k, lane);
-        else
-            select_hash_wave(a.token_ids, a.wt.table, t, d.vocab, d.table_k, d.E, d.k, rs.ids + t * d.k,
-                             rs.w + t * d.k, a.ws.ctl + kCtlFlags,
-                             d.route == kRouteHashScored ? a.ws.scores + (int64_t)t * d.E : nullptr, lane);
-    }
+    const int P4 = (P + 3) & ~3;
+    if (tid >= P && tid < P4) rs.ids[tid] = 0x7fffffff;
     __syncthreads();
+    const int4 *__restrict__ ids4 = reinterpret_cast<const int4 *>(rs.ids);
     if (tid < P) {
         const int e = rs.ids[tid];
         int rank = 0;
-        for (int q = 0; q < P; ++q) {
-            const int f = rs.ids[q];
-            rank += (f < e) || (f == e && q < tid);
+#pragma unroll 4
+        for (int q4 = 0; q4 < P4 / 4; ++q4) {
+            const int4 f = ids4[q4];
+            const int q = 4 * q4;
+            rank += (f.x < e) || (f.x == e && q < tid);
+            rank += (f.y < e) || (f.y == e && q + 1 < tid);
+            rank += (f.z < e) || (f.z == e && q + 2 < tid);
+            rank += (f.w < e) || (f.w == e && q + 3 < tid);
         }
         rs.perm[rank] = tid;
         a.ws.ids[tid] = e;
@@ -180,9 +208,11 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
     }
     for (int e = tid; e < d.E; e += 256) {
         int c = 0, below = 0;
-        for (int p = 0; p < P; ++p) {
-            c += rs.ids[p] == e;
-            below += rs.ids[p] < e;
+#pragma unroll 4
+        for (int q4 = 0; q4 < P4 / 4; ++q4) {
+            const int4 f = ids4[q4];
+            c += (f.x == e) + (f.y == e) + (f.z == e) + (f.w == e);
+            below += (f.x < e) + (f.y < e) + (f.z < e) + (f.w < e);
         }
         a.ws.counts[e] = c;
         a.ws.offsets[e] = below;

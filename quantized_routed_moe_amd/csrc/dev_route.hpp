@@ -110,18 +110,27 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // write the result.
 //  PER candidate slots per lane (64 * PER >= E); slots past E hold 0, below
 //  every key image, and are never taken.
+// The token's keys (as order-preserving images) and scores, PER per lane.
 template <int PER>
-__device__ void select_keys_per(const float *__restrict__ krow, const float *__restrict__ srow, int E, int k,
-                                int &my_id, float &my_w, int lane) {
+struct KeyRegs {
     uint32_t u[PER];
     float s[PER];
+    __device__ __forceinline__ void load(const float *__restrict__ krow, const float *__restrict__ srow, int E,
+                                         int lane) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        const bool ok = e < E;
-        u[i] = ok ? key_order(krow[e]) : 0u;
-        s[i] = ok ? srow[e] : 0.0f;
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane + 64 * i;
+            const bool ok = e < E;
+            u[i] = ok ? key_order(krow[e]) : 0u;
+            s[i] = ok ? srow[e] : 0.0f;
+        }
     }
+};
+
+template <int PER>
+__device__ void select_keys_from(KeyRegs<PER> r, int k, int &my_id, float &my_w, int lane) {
+    uint32_t *u = r.u;
+    const float *s = r.s;
     my_id = 0;
     float my_s = 0.0f, S = 0.0f;
     for (int r = 0; r < k; ++r) {
@@ -153,6 +162,14 @@ __device__ void select_keys_per(const float *__restrict__ krow, const float *__r
         }
     }
     my_w = my_s / S;
+}
+
+template <int PER>
+__device__ __forceinline__ void select_keys_per(const float *__restrict__ krow, const float *__restrict__ srow, int E,
+                                                int k, int &my_id, float &my_w, int lane) {
+    KeyRegs<PER> r;
+    r.load(krow, srow, E, lane);
+    select_keys_from<PER>(r, k, my_id, my_w, lane);
 }
 
 // Lane r < k of the calling wave receives the rank-r expert id and weight.
@@ -206,6 +223,42 @@ __device__ __forceinline__ void select_hash_regs(const int32_t *__restrict__ tok
         for (int j = 0; j < 8; ++j)
             if (j < k) S += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), j));
         if (lane < k) w_out = sc / S;
+    }
+}
+
+// Hash routing of several tokens per wave, eight lanes per token: lane j < k
+// of token t's group takes entry j of the token's table row and its weight,
+// with the same clamping, flags and arithmetic as select_hash_regs (S summed
+// in table order, the group's lane order).  scores, when given, is [T][E].
+__device__ __forceinline__ void select_hash_group8(const int32_t *__restrict__ token_ids,
+                                                   const int32_t *__restrict__ table, int t, bool valid, int vocab,
+                                                   int row_k, int E, int k, int &id_out, float &w_out,
+                                                   int32_t *flags, const float *__restrict__ scores, int lane) {
+    const int j = lane & 7;
+    int id = valid ? token_ids[t] : 0;
+    if (id < 0 || id >= vocab) {
+        if (j == 0) atomicOr(flags, 1);
+        id = 0;
+    }
+    const bool mine = valid && j < k;
+    int e = 0;
+    if (mine) {
+        e = table[(int64_t)id * row_k + j];
+        if (e < 0 || e >= E) {
+            atomicOr(flags, 2);
+            e = 0;
+        }
+    }
+    id_out = e;
+    w_out = mine ? 1.0f / (float)k : 0.0f;
+    if (scores) {
+        const float sc = mine ? scores[(int64_t)t * E + e] : 0.0f;
+        const int base = lane & ~7;
+        float S = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < k) S += __shfl(sc, base + i);
+        if (mine) w_out = sc / S;
     }
 }
 

@@ -14,7 +14,8 @@
 
 namespace qrmoe {
 
-// SKIP_SHARED: decode batches, whose shared-expert gate/up ran in the front kernel.
+// SKIP_SHARED: decode batches, whose shared-expert gate/up ran in the front
+// kernel; the shared groups' workgroups quantize that h instead.
 template <int K, int FMT, bool DUMP, bool SKIP_SHARED>
 __global__ __launch_bounds__(256) void gateup_vec_kernel(LayerArgs a) {
     __shared__ VecSmem<K, kVecTok> sm;
@@ -23,7 +24,25 @@ __global__ __launch_bounds__(256) void gateup_vec_kernel(LayerArgs a) {
     const int4 grp = a.ws.groups[g];  // in the allocation for every g of the grid; used only when g < ngroups
     if (g >= ngroups) return;
     const bool shared = grp.x == a.d.E;
-    if (SKIP_SHARED && shared) return;
+    static_assert(kVecTok * kVecRows == 256, "one thread per (token, row) of an h block");
+    if (SKIP_SHARED && shared) {
+        // the front kernel left the shared expert's h in fp32: quantize this
+        // workgroup's 32-row block of it for the group's tokens (one token
+        // per 32 lanes; the same arithmetic as every h quantization)
+        const int tid = threadIdx.x, tok = tid / kVecRows, i = tid % kVecRows;
+        const int r = blockIdx.x * kVecRows + i;
+        const bool ok = tok < grp.z;
+        const int64_t p = (int64_t)a.d.T * a.d.k + grp.y + (ok ? tok : 0);
+        const float v = ok ? a.ws.h[p * a.d.F + r] : 0.0f;
+        const float amax = group_max<32>(fabsf(v));
+        if (ok) {
+            const float dsc = quant_scale(amax);
+            const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
+            a.ws.hq[p * a.d.F + r] = (int8_t)quant_code(v, inv);
+            if (i == 0) a.ws.hd[p * (a.d.F / 32) + r / 32] = dsc;
+        }
+        return;
+    }
     const int tid = threadIdx.x;
     const int r0 = blockIdx.x * kVecRows;
     // the group's pairs are requested before the weight rows (a wave waits for
