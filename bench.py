@@ -151,14 +151,12 @@ def stage_model(cfg, qr, u_avg):
     st = {}
     if T <= 32:
         sel = (2 * T * E * 4 if has_router else T * 4) + T * k * 12
-        if T == 1:  # selection and the shared expert's gate/up run in the gate/up kernel
-            st["route"] = router + x32 + xq + rout
+        st["route"] = router + x32 + xq + rout
+        if T == 1:  # selection runs in the gate/up kernel
             st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P) + sel
         else:
-            st["route"] = router + x32 + xq + rout + sh * (2 * mq8_gu + T * F * 4)
-            sel += sh * (T * F * 4 + hq(T))
             st["select"] = sel
-            st["gateup"] = u_avg * 2 * mr_gu + xq + hq(Pr)
+            st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P)
         if T == 1:
             st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + x32
         else:

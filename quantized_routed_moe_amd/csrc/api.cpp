@@ -57,7 +57,7 @@ int64_t max_groups(const moe_shape *s, int64_t T, int64_t G) {
 }
 
 struct Layout {
-    size_t ctl, logits, scores, keys, ids, w, xq, xd, xs16, counts, offsets, perm, groups, hq, hd, y, h, total;
+    size_t ctl, logits, scores, keys, ids, w, xq, xd, xs16, counts, offsets, perm, groups, hq, hd, y, total;
 };
 
 
@@ -91,9 +91,6 @@ Layout make_layout(const moe_shape *s, int64_t T) {
     L.hq = take(P * F);
     L.hd = take(P * (F / 32) * 4);
     L.y = take(P * H * 4);
-    // fp32 h of decode batches; sized for min(T, decode limit) so the total stays monotone in T
-    const int64_t Td = T < kDecodeMaxT ? T : kDecodeMaxT;
-    L.h = take((Td * k + (s->has_shared ? Td : 0)) * F * 4);
     L.total = o;
     return L;
 }
@@ -191,7 +188,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
               (float *)(base + L.w), (int8_t *)(base + L.xq), (float *)(base + L.xd),
               (int32_t *)(base + L.xs16), (int32_t *)(base + L.counts), (int32_t *)(base + L.offsets),
               (int32_t *)(base + L.perm), (int4 *)(base + L.groups), (int8_t *)(base + L.hq),
-              (float *)(base + L.hd), (float *)(base + L.y), (float *)(base + L.h), (float *)(base + L.scores),
+              (float *)(base + L.hd), (float *)(base + L.y), (float *)(base + L.scores),
               (float *)(base + L.keys)};
     const bool dump = dbg && (dbg->gate_sums || dbg->up_sums || dbg->down_sums);
     const bool q2 = shape->routed_fmt == MOE_FMT_Q2_256;
@@ -209,14 +206,14 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
     const int64_t mg = max_groups(shape, T, kVecTok);
     a.group_tok = kVecTok;
     if (T <= kDecodeMaxT) {
-        run(MOE_STAGE_ROUTE, [&] { return launch_decode_front(a, dump, s); });
+        run(MOE_STAGE_ROUTE, [&] { return launch_decode_front(a, s); });
         if (T == 1) {
             // one token: the selection runs inside the gate/up workgroups
             run(MOE_STAGE_GATEUP, [&] { return launch_decode_gateup1(a, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_decode_down1(a, dump, s); });
         } else {
             run(MOE_STAGE_SELECT, [&] { return launch_decode_select(a, s); });
-            run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, true, dump, s); });
+            run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
             run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
         }
@@ -234,7 +231,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
             run(MOE_STAGE_GATEUP, [&] { return launch_gateup_mfma(a, (int)tiles, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_down_mfma(a, (int)tiles, dump, s); });
         } else {
-            run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, false, dump, s); });
+            run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
         }
         run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });

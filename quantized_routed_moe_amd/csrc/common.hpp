@@ -65,7 +65,6 @@ struct Ws {
     int8_t *hq;
     float *hd;
     float *y;        // [P][H] weighted expert outputs (w already applied)
-    float *h;        // [P][F] SwiGLU output before quantization (decode batches)
     float *scores;   // [T][E] sigmoid scores
     float *keys;     // [T][E] selection keys (score + bias)
 };
@@ -315,7 +314,7 @@ hipError_t launch_pack(int fmt, const uint8_t *canon, uint8_t *packed, int64_t n
 hipError_t launch_check_table(const int32_t *table, int32_t vocab, int32_t k, int32_t E, int32_t *result,
                               hipStream_t s);
 hipError_t launch_ws_init(int32_t *ctl, int64_t n_words, hipStream_t s);
-hipError_t launch_decode_front(const LayerArgs &a, bool dump, hipStream_t s);
+hipError_t launch_decode_front(const LayerArgs &a, hipStream_t s);
 hipError_t launch_decode_select(const LayerArgs &a, hipStream_t s);
 hipError_t launch_select_sort(const LayerArgs &a, hipStream_t s);
 hipError_t launch_decode_gateup1(const LayerArgs &a, bool dump, hipStream_t s);
@@ -324,7 +323,7 @@ hipError_t launch_quant(const LayerArgs &a, hipStream_t s);
 hipError_t launch_logits(const LayerArgs &a, hipStream_t s);
 hipError_t launch_select(const LayerArgs &a, hipStream_t s);
 hipError_t launch_sort(const LayerArgs &a, hipStream_t s);
-hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool skip_shared, bool dump, hipStream_t s);
+hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool dump, hipStream_t s);
 hipError_t launch_down_vec(const LayerArgs &a, int max_groups, bool dump, hipStream_t s);
 hipError_t launch_combine(const LayerArgs &a, hipStream_t s);
 hipError_t launch_gateup_mfma(const LayerArgs &a, int max_tiles, bool dump, hipStream_t s);

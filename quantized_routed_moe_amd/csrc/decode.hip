@@ -2,12 +2,10 @@
 //
 //  front   quantize x and compute the router logits, scores and selection
 //          keys (learned layers: one workgroup per logit, the four waves each
-//          sum a quarter of the adjacent-pair tree); for 2..32 tokens further
-//          workgroups stream the shared expert's gate/up rows, which need no
-//          routing, leaving its h in fp32.
+//          sum a quarter of the adjacent-pair tree).
 //  select  one workgroup: top-k or hash selection, sort, work list.
-//  gateup  routed experts' gate/up + SwiGLU + h quantization, and the
-//          quantization of the shared expert's h (expert_vec.hip).
+//  gateup  T == 1: below.  T > 1: gate/up + SwiGLU + h quantization of the
+//          routed and shared groups of the work list (expert_vec.hip).
 //  down    T == 1: one kernel computes every output row from all selected
 //          experts at once (each wave holds the row of every expert in
 //          registers, requested before anything else) and sums w * y in
@@ -24,77 +22,50 @@ namespace qrmoe {
 
 // ------------------------------------------------------------------ front
 template <int H>
-struct FrontSmem {
-    VecSmem<H, kVecTok> vs;
-    double part[4];
-};
-
-template <int H, bool DUMP>
 __global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_lead) {
-    __shared__ FrontSmem<H> sm;
+    __shared__ double part[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
-    if ((int)blockIdx.x < n_lead) {
-        const int nblk = d.T * (H / 32);
-        for (int b = blockIdx.x * 256 + tid; b < nblk; b += n_lead * 256)
-            quant_one_block(a.x, a.ws.xq, a.ws.xd, d.fmt == kFmtQ2 ? a.ws.xs16 : nullptr, b);
-        if (d.route == kRouteHash) return;  // no router
-        const int nlog = d.T * d.E;
-        if constexpr (H >= 256) {
-            // one logit per workgroup; wave w sums elements [w*H/4, (w+1)*H/4)
-            constexpr int SEG = H / 256;
-            for (int le = blockIdx.x; le < nlog; le += n_lead) {
-                const int t = le / d.E, e = le % d.E;
-                const int off = wave * (H / 4) + lane * SEG;
-                const double v = wave_sum_f64(
-                    segment_tree<SEG>(a.x + (int64_t)t * H + off, a.wt.router_w + (int64_t)e * H + off));
-                if (lane == 0) sm.part[wave] = v;
-                __syncthreads();
-                if (tid == 0) {
-                    const float l = (float)((sm.part[0] + sm.part[1]) + (sm.part[2] + sm.part[3]));
-                    a.ws.logits[le] = l;
-                    score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
-                }
-                __syncthreads();
+    const int nblk = d.T * (H / 32);
+    for (int b = blockIdx.x * 256 + tid; b < nblk; b += n_lead * 256)
+        quant_one_block(a.x, a.ws.xq, a.ws.xd, d.fmt == kFmtQ2 ? a.ws.xs16 : nullptr, b);
+    if (d.route == kRouteHash) return;  // no router
+    const int nlog = d.T * d.E;
+    if constexpr (H >= 256) {
+        // one logit per workgroup; wave w sums elements [w*H/4, (w+1)*H/4)
+        constexpr int SEG = H / 256;
+        for (int le = blockIdx.x; le < nlog; le += n_lead) {
+            const int t = le / d.E, e = le % d.E;
+            const int off = wave * (H / 4) + lane * SEG;
+            const double v =
+                wave_sum_f64(segment_tree<SEG>(a.x + (int64_t)t * H + off, a.wt.router_w + (int64_t)e * H + off));
+            if (lane == 0) part[wave] = v;
+            __syncthreads();
+            if (tid == 0) {
+                const float l = (float)((part[0] + part[1]) + (part[2] + part[3]));
+                a.ws.logits[le] = l;
+                score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
             }
-        } else {
-            for (int le = blockIdx.x * 4 + wave; le < nlog; le += n_lead * 4) {
-                const int t = le / d.E, e = le % d.E;
-                const float l = wave_logit<H>(a.x + (int64_t)t * H, a.wt.router_w + (int64_t)e * H, lane);
-                if (lane == 0) {
-                    a.ws.logits[le] = l;
-                    score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
-                }
+            __syncthreads();
+        }
+    } else {
+        for (int le = blockIdx.x * 4 + wave; le < nlog; le += n_lead * 4) {
+            const int t = le / d.E, e = le % d.E;
+            const float l = wave_logit<H>(a.x + (int64_t)t * H, a.wt.router_w + (int64_t)e * H, lane);
+            if (lane == 0) {
+                a.ws.logits[le] = l;
+                score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
             }
         }
-        return;
     }
-    // shared expert: ROWS rows x up to 8 tokens; quantize those tokens' x into LDS
-    constexpr int ROWS = GuRows<H, kFmtQ8>::v;
-    const int s = blockIdx.x - n_lead, nrc = d.F / ROWS;
-    const int rc = s % nrc, t0 = (s / nrc) * kVecTok;
-    const int cnt = min(kVecTok, d.T - t0);
-    // each thread's first x block is requested before the weight rows
-    QBlock xb;
-    const bool first = tid < cnt * (H / 32);
-    if (first) xb.load(a.x + (int64_t)(t0 + tid / (H / 32)) * H, tid % (H / 32));
-    gateup_rows<H, kFmtQ8, kVecTok, ROWS, false, DUMP>(a, sm.vs, a.wt.sh_gate, a.wt.sh_up, cnt, rc * ROWS, [&] {
-        if (first) xb.store(sm.vs.aq[tid / (H / 32)], sm.vs.ad[tid / (H / 32)], nullptr, tid % (H / 32));
-        for (int b = tid + 256; b < cnt * (H / 32); b += 256) {
-            const int tok = b / (H / 32), blk = b % (H / 32);
-            quant_one_block(a.x + (int64_t)(t0 + tok) * H, sm.vs.aq[tok], sm.vs.ad[tok], nullptr, blk);
-        }
-        if (tid < cnt) sm.vs.pair[tid] = d.T * d.k + t0 + tid;
-        __syncthreads();
-    });
 }
 
 // ----------------------------------------------------------------- select
 // One workgroup: top-k (or hash lookup) of every token, stable sort of the
 // P = T*k <= 256 pairs by expert (rank = number of pairs with a smaller
 // expert, or the same expert and a smaller pair index), and the work list
-// (each expert's pairs cut into runs of at most kVecTok, experts ascending,
-// then the shared expert's token runs).
+// (the shared expert's token runs, then each expert's pairs cut into runs
+// of at most kVecTok, experts ascending).
 struct SelectSmem {
     alignas(16) int32_t ids[kDecodeMaxT * 8];  // padded to a multiple of 4 with INT_MAX (counted nowhere)
     float w[kDecodeMaxT * 8];
@@ -130,8 +101,6 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int P = d.T * d.k;
-    // (the shared expert's h, fp32 from the front kernel, is quantized by the
-    // gate/up kernel's otherwise idle shared-group workgroups)
     if (d.route == kRouteLearned) {
         if (d.E <= 64) select_learned_tokens<1>(a, rs, wave, lane);
         else if (d.E <= 128) select_learned_tokens<2>(a, rs, wave, lane);
@@ -194,14 +163,16 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
     if (flag) rs.gpos[inc - 1] = tid;
     if (tid == 255) rs.ngroups = inc;
     __syncthreads();
+    // the shared expert's token runs first: their workgroups carry the most
+    // tokens, so they start with the kernel instead of forming its tail
     const int G = rs.ngroups;
-    for (int g = tid; g < G; g += 256) {
-        const int gs = rs.gpos[g], ge = g + 1 < G ? rs.gpos[g + 1] : P;
-        a.ws.groups[g] = make_int4(rs.ids[rs.perm[gs]], gs, ge - gs, rs.perm[gs]);
-    }
     const int ns = d.has_shared ? (d.T + kVecTok - 1) / kVecTok : 0;
     for (int j = tid; j < ns; j += 256)
-        a.ws.groups[G + j] = make_int4(d.E, j * kVecTok, min(kVecTok, d.T - j * kVecTok), P + j * kVecTok);
+        a.ws.groups[j] = make_int4(d.E, j * kVecTok, min(kVecTok, d.T - j * kVecTok), P + j * kVecTok);
+    for (int g = tid; g < G; g += 256) {
+        const int gs = rs.gpos[g], ge = g + 1 < G ? rs.gpos[g + 1] : P;
+        a.ws.groups[ns + g] = make_int4(rs.ids[rs.perm[gs]], gs, ge - gs, rs.perm[gs]);
+    }
     if (tid == 0) {
         a.ws.ctl[kCtlGroups] = G + ns;
         a.ws.offsets[d.E] = P;
@@ -270,7 +241,7 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
             sm.pair[0] = d.k;
             sm.row[0] = 0;
         }
-        gateup_rows<K, kFmtQ8, kVecTok, SR, true, DUMP, NW>(
+        gateup_rows<K, kFmtQ8, kVecTok, SR, DUMP, NW>(
             a, sm, a.wt.sh_gate, a.wt.sh_up, 1, ((slot - d.k) * gridDim.x + blockIdx.x) * SR, [&] {
                 for (int i = tid; i < K / 16; i += 64 * NW) {
                     reinterpret_cast<int4 *>(sm.aq[0])[i] = reinterpret_cast<const int4 *>(a.ws.xq)[i];
@@ -373,7 +344,7 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
         if (FMT == kFmtQ2) sm.as16[tok][c] = sm.as16[0][c];
     }
     const int64_t mb = mat_bytes(FMT, d.F, K);
-    gateup_rows<K, FMT, kVecTok, ROWS, true, DUMP, NW>(a, sm, a.wt.gate + e * mb, a.wt.up + e * mb, cnt,
+    gateup_rows<K, FMT, kVecTok, ROWS, DUMP, NW>(a, sm, a.wt.gate + e * mb, a.wt.up + e * mb, cnt,
                                                                blockIdx.x * ROWS, [&] { __syncthreads(); });
 }
 
@@ -502,7 +473,7 @@ __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
 }
 
 // ------------------------------------------------------------- launchers
-template <int H, bool DUMP>
+template <int H>
 static hipError_t front_h(const LayerArgs &a, hipStream_t s) {
     const Dims &d = a.d;
     const int nq = (d.T * (H / 32) + 255) / 256;
@@ -512,20 +483,18 @@ static hipError_t front_h(const LayerArgs &a, hipStream_t s) {
         n_lead = nl > nq ? nl : nq;
     }
     if (n_lead > 4096) n_lead = 4096;
-    // one token: the shared expert's gate/up runs in the one-token gate/up kernel instead
-    const int ns = d.has_shared && d.T > 1 ? (d.F / GuRows<H, kFmtQ8>::v) * ((d.T + kVecTok - 1) / kVecTok) : 0;
-    klaunch(decode_front_kernel<H, DUMP>, dim3(n_lead + ns), dim3(256), s, a, n_lead);
+    klaunch(decode_front_kernel<H>, dim3(n_lead), dim3(256), s, a, n_lead);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_front(const LayerArgs &a, bool dump, hipStream_t s) {
+hipError_t launch_decode_front(const LayerArgs &a, hipStream_t s) {
     switch (a.d.H) {
-        case 128: return dump ? front_h<128, true>(a, s) : front_h<128, false>(a, s);
-        case 256: return dump ? front_h<256, true>(a, s) : front_h<256, false>(a, s);
-        case 512: return dump ? front_h<512, true>(a, s) : front_h<512, false>(a, s);
-        case 1024: return dump ? front_h<1024, true>(a, s) : front_h<1024, false>(a, s);
-        case 2048: return dump ? front_h<2048, true>(a, s) : front_h<2048, false>(a, s);
-        case 4096: return dump ? front_h<4096, true>(a, s) : front_h<4096, false>(a, s);
+        case 128: return front_h<128>(a, s);
+        case 256: return front_h<256>(a, s);
+        case 512: return front_h<512>(a, s);
+        case 1024: return front_h<1024>(a, s);
+        case 2048: return front_h<2048>(a, s);
+        case 4096: return front_h<4096>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -193,18 +193,16 @@ struct GuDepth {
 };
 
 // Gate/up of one expert for rows r0..r0+ROWS-1 and the cnt staged tokens,
-// then SwiGLU.  QUANT: quantize the 32-row h block of every token here
-// (ROWS == 32) into hq/hd; otherwise store h in fp32 for the consumer to
-// quantize (the same values give the same codes wherever they are
-// quantized).  sm.pair[] names the output pair of each token.
+// then SwiGLU, and the quantization of each token's 32-row h blocks into
+// hq/hd.  sm.pair[] names the output pair of each token.
 //
 // Each wave keeps the rows of the next DEPTH - 1 passes in flight (a ring of
 // DEPTH gate and up rows, indexed at compile time).  The first DEPTH - 1 are
 // requested before `stage()` (the caller's activation staging, which ends
 // with a barrier), so weight streaming starts as soon as the expert is known.
-// NW waves per workgroup; with QUANT the workgroup's NW*64 threads cover (at
-// least) NTOK tokens x ROWS rows of h (ROWS a multiple of the 32-row h block).
-template <int K, int FMT, int NTOK, int ROWS, bool QUANT, bool DUMP, int NW = 4, class Stage>
+// NW waves per workgroup, whose NW*64 threads cover (at least) NTOK tokens x
+// ROWS rows of h (ROWS a multiple of the 32-row h block).
+template <int K, int FMT, int NTOK, int ROWS, bool DUMP, int NW = 4, class Stage>
 __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint8_t *__restrict__ gmat,
                             const uint8_t *__restrict__ umat, int cnt, int r0, Stage stage) {
     using G = Geo<K, FMT>;
@@ -212,7 +210,7 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
     constexpr int PASSES = ROWS / (NW * G::RPW);
     constexpr int DEPTH = GuDepth<K, FMT>::v < PASSES + 1 ? GuDepth<K, FMT>::v : PASSES + 1;
     static_assert(PASSES >= 1 && ROWS % (NW * G::RPW) == 0, "row geometry");
-    static_assert(!QUANT || (ROWS % kVecRows == 0 && ROWS <= 2 * kVecRows && NW * 64 >= NTOK * ROWS), "h blocks");
+    static_assert(ROWS % kVecRows == 0 && ROWS <= 2 * kVecRows && NW * 64 >= NTOK * ROWS, "h blocks");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
     const int seg = lane % G::L, rsub = lane / G::L;
@@ -245,27 +243,19 @@ __device__ void gateup_rows(const LayerArgs &a, VecSmem<K, NTOK> &sm, const uint
             }
             const float gp = group_sum<G::L>(lane_dot<K, G::L>(g0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, dg));
             const float up = group_sum<G::L>(lane_dot<K, G::L>(u0, sm.aq[tok], sm.ad[tok], sm.as16[tok], seg, du));
-            if (seg == 0) {
-                const float hv = swiglu(gp, up);
-                if constexpr (QUANT)
-                    sm.h[tok][row_local] = hv;
-                else
-                    a.ws.h[(int64_t)sm.pair[tok] * d.F + r] = hv;
-            }
+            if (seg == 0) sm.h[tok][row_local] = swiglu(gp, up);
         }
     }
-    if constexpr (QUANT) {
-        __syncthreads();
-        const int tok = tid / ROWS, i = tid % ROWS;  // 32 consecutive lanes = one h block of one token (tok < NTOK...)
-        const float v = tok < cnt ? sm.h[tok][i] : 0.0f;
-        const float amax = group_max<32>(fabsf(v));
-        if (tok < cnt) {
-            const float dsc = quant_scale(amax);
-            const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
-            const int p = sm.pair[tok];
-            a.ws.hq[(int64_t)p * d.F + r0 + i] = (int8_t)quant_code(v, inv);
-            if (i % 32 == 0) a.ws.hd[(int64_t)p * (d.F / 32) + (r0 + i) / 32] = dsc;
-        }
+    __syncthreads();
+    const int tok = tid / ROWS, i = tid % ROWS;  // 32 consecutive lanes = one h block of one token (tok < NTOK...)
+    const float v = tok < cnt ? sm.h[tok][i] : 0.0f;
+    const float amax = group_max<32>(fabsf(v));
+    if (tok < cnt) {
+        const float dsc = quant_scale(amax);
+        const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
+        const int p = sm.pair[tok];
+        a.ws.hq[(int64_t)p * d.F + r0 + i] = (int8_t)quant_code(v, inv);
+        if (i % 32 == 0) a.ws.hd[(int64_t)p * (d.F / 32) + (r0 + i) / 32] = dsc;
     }
 }
 

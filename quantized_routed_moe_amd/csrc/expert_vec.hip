@@ -14,9 +14,7 @@
 
 namespace qrmoe {
 
-// SKIP_SHARED: decode batches, whose shared-expert gate/up ran in the front
-// kernel; the shared groups' workgroups quantize that h instead.
-template <int K, int FMT, bool DUMP, bool SKIP_SHARED>
+template <int K, int FMT, bool DUMP>
 __global__ __launch_bounds__(256) void gateup_vec_kernel(LayerArgs a) {
     __shared__ VecSmem<K, kVecTok> sm;
     const int g = blockIdx.y;
@@ -24,25 +22,6 @@ __global__ __launch_bounds__(256) void gateup_vec_kernel(LayerArgs a) {
     const int4 grp = a.ws.groups[g];  // in the allocation for every g of the grid; used only when g < ngroups
     if (g >= ngroups) return;
     const bool shared = grp.x == a.d.E;
-    static_assert(kVecTok * kVecRows == 256, "one thread per (token, row) of an h block");
-    if (SKIP_SHARED && shared) {
-        // the front kernel left the shared expert's h in fp32: quantize this
-        // workgroup's 32-row block of it for the group's tokens (one token
-        // per 32 lanes; the same arithmetic as every h quantization)
-        const int tid = threadIdx.x, tok = tid / kVecRows, i = tid % kVecRows;
-        const int r = blockIdx.x * kVecRows + i;
-        const bool ok = tok < grp.z;
-        const int64_t p = (int64_t)a.d.T * a.d.k + grp.y + (ok ? tok : 0);
-        const float v = ok ? a.ws.h[p * a.d.F + r] : 0.0f;
-        const float amax = group_max<32>(fabsf(v));
-        if (ok) {
-            const float dsc = quant_scale(amax);
-            const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
-            a.ws.hq[p * a.d.F + r] = (int8_t)quant_code(v, inv);
-            if (i == 0) a.ws.hd[p * (a.d.F / 32) + r / 32] = dsc;
-        }
-        return;
-    }
     const int tid = threadIdx.x;
     const int r0 = blockIdx.x * kVecRows;
     // the group's pairs are requested before the weight rows (a wave waits for
@@ -60,11 +39,11 @@ __global__ __launch_bounds__(256) void gateup_vec_kernel(LayerArgs a) {
         __syncthreads();
     };
     if (shared) {
-        gateup_rows<K, kFmtQ8, kVecTok, kVecRows, true, DUMP>(a, sm, a.wt.sh_gate, a.wt.sh_up, grp.z, r0,
+        gateup_rows<K, kFmtQ8, kVecTok, kVecRows, DUMP>(a, sm, a.wt.sh_gate, a.wt.sh_up, grp.z, r0,
                                                              [&] { stage(false); });
     } else {
         const int64_t mb = mat_bytes(FMT, a.d.F, K);
-        gateup_rows<K, FMT, kVecTok, kVecRows, true, DUMP>(a, sm, a.wt.gate + grp.x * mb, a.wt.up + grp.x * mb, grp.z,
+        gateup_rows<K, FMT, kVecTok, kVecRows, DUMP>(a, sm, a.wt.gate + grp.x * mb, a.wt.up + grp.x * mb, grp.z,
                                                           r0, [&] { stage(FMT == kFmtQ2); });
     }
 }
@@ -184,30 +163,24 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
 }
 
 // ------------------------------------------------------------- launchers
-template <int FMT, bool DUMP, bool SKIP>
+template <int FMT, bool DUMP>
 static hipError_t gateup_k(const LayerArgs &a, dim3 grid, hipStream_t s) {
     switch (a.d.H) {
-        case 128: if constexpr (FMT == kFmtQ8) { klaunch(gateup_vec_kernel<128, FMT, DUMP, SKIP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
-        case 256: if constexpr (FMT == kFmtQ8) { klaunch(gateup_vec_kernel<256, FMT, DUMP, SKIP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
-        case 512: klaunch(gateup_vec_kernel<512, FMT, DUMP, SKIP>, grid, 256, s, a); break;
-        case 1024: klaunch(gateup_vec_kernel<1024, FMT, DUMP, SKIP>, grid, 256, s, a); break;
-        case 2048: klaunch(gateup_vec_kernel<2048, FMT, DUMP, SKIP>, grid, 256, s, a); break;
-        case 4096: klaunch(gateup_vec_kernel<4096, FMT, DUMP, SKIP>, grid, 256, s, a); break;
+        case 128: if constexpr (FMT == kFmtQ8) { klaunch(gateup_vec_kernel<128, FMT, DUMP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
+        case 256: if constexpr (FMT == kFmtQ8) { klaunch(gateup_vec_kernel<256, FMT, DUMP>, grid, 256, s, a); break; } return hipErrorInvalidValue;
+        case 512: klaunch(gateup_vec_kernel<512, FMT, DUMP>, grid, 256, s, a); break;
+        case 1024: klaunch(gateup_vec_kernel<1024, FMT, DUMP>, grid, 256, s, a); break;
+        case 2048: klaunch(gateup_vec_kernel<2048, FMT, DUMP>, grid, 256, s, a); break;
+        case 4096: klaunch(gateup_vec_kernel<4096, FMT, DUMP>, grid, 256, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <int FMT, bool SKIP>
-static hipError_t gateup_d(const LayerArgs &a, dim3 grid, bool dump, hipStream_t s) {
-    return dump ? gateup_k<FMT, true, SKIP>(a, grid, s) : gateup_k<FMT, false, SKIP>(a, grid, s);
-}
-
-hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool skip_shared, bool dump, hipStream_t s) {
+hipError_t launch_gateup_vec(const LayerArgs &a, int max_groups, bool dump, hipStream_t s) {
     dim3 grid(a.d.F / kVecRows, max_groups);
-    if (a.d.fmt == kFmtQ8)
-        return skip_shared ? gateup_d<kFmtQ8, true>(a, grid, dump, s) : gateup_d<kFmtQ8, false>(a, grid, dump, s);
-    return skip_shared ? gateup_d<kFmtQ2, true>(a, grid, dump, s) : gateup_d<kFmtQ2, false>(a, grid, dump, s);
+    if (a.d.fmt == kFmtQ8) return dump ? gateup_k<kFmtQ8, true>(a, grid, s) : gateup_k<kFmtQ8, false>(a, grid, s);
+    return dump ? gateup_k<kFmtQ2, true>(a, grid, s) : gateup_k<kFmtQ2, false>(a, grid, s);
 }
 
 template <int FMT, bool DUMP>

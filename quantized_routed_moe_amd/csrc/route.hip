@@ -23,8 +23,9 @@ namespace qrmoe {
 
 // ------------------------------------------------- sort + work-list build
 // Stable counting sort of the P = T*k pairs by expert, then the work list:
-// each expert's pairs cut into groups of at most G, followed by the shared
-// expert's tokens cut the same way.  Up to kSortOneWg pairs it runs in ONE
+// the shared expert's tokens cut into groups of at most G (full groups, so
+// their workgroups start first rather than trail), followed by each
+// expert's pairs cut the same way.  Up to kSortOneWg pairs it runs in ONE
 // workgroup of 256 threads; larger batches take three kernels: per-chunk
 // histograms, one workgroup for the prefix sums and the work list, and a
 // per-chunk stable scatter.
@@ -91,16 +92,16 @@ __device__ void write_work_list(const Dims &d, const Ws &ws, int G, SortSmem &sm
     __syncthreads();
     block_excl_scan(sm.nch, sm.gbase, E, sm.tmp, &sm.total);
     const int routed_groups = sm.total;
+    const int shared_groups = d.has_shared ? (d.T + G - 1) / G : 0;
+    for (int j = tid; j < shared_groups; j += 256)
+        ws.groups[j] = make_int4(E, j * G, min(G, d.T - j * G), 0);
     for (int e = tid; e < E; e += 256) {
         const int c = sm.cnt[e];
         for (int j = 0; j < sm.nch[e]; ++j) {
             const int n = min(G, c - j * G);
-            ws.groups[sm.gbase[e] + j] = make_int4(e, sm.off[e] + j * G, n, 0);
+            ws.groups[shared_groups + sm.gbase[e] + j] = make_int4(e, sm.off[e] + j * G, n, 0);
         }
     }
-    const int shared_groups = d.has_shared ? (d.T + G - 1) / G : 0;
-    for (int j = tid; j < shared_groups; j += 256)
-        ws.groups[routed_groups + j] = make_int4(E, j * G, min(G, d.T - j * G), 0);
     if (tid == 0) ws.ctl[kCtlGroups] = routed_groups + shared_groups;
 }
 
