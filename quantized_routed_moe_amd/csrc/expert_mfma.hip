@@ -213,6 +213,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
         st.store(sm);
         __syncthreads();
         if (c + 1 < NC) st.load(c + 1);
+        // block kb's int8 MFMA is issued before block kb-1's conversions and fmas
+        auto block_mfma = [&](int kb) {
+            const i32x4 av = *reinterpret_cast<const i32x4 *>(&sm.A[wm * 32 + n][kb * 32 + 16 * half]);
+            const i32x4 bv = *reinterpret_cast<const i32x4 *>(&sm.B[brow_lds][kb * 32 + 16 * half]);
+            const v16i zero = {};
+            return __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
+        };
+        v16i cnext = block_mfma(0);
 #pragma unroll
         for (int kb = 0; kb < kKC; kb += 2) {
             // scale products of blocks kb (registers 0..15) and kb+1 (16..31)
@@ -223,10 +231,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int b = c * kKC + kb + j;
-                const i32x4 av = *reinterpret_cast<const i32x4 *>(&sm.A[wm * 32 + n][(kb + j) * 32 + 16 * half]);
-                const i32x4 bv = *reinterpret_cast<const i32x4 *>(&sm.B[brow_lds][(kb + j) * 32 + 16 * half]);
-                const v16i zero = {};
-                const v16i cv = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
+                const v16i cv = cnext;
+                if (kb + j + 1 < kKC) cnext = block_mfma(kb + j + 1);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[i] = __fmaf_rn((float)cv[i], ps[16 * j + i], acc[i]);
                 if (DUMP && (col % a.dump.stride == 0)) {
