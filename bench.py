@@ -130,8 +130,8 @@ def stage_model(cfg, qr, u_avg):
 
     Bytes count what a stage must move at least once: the weights of every
     expert that receives a token, router weights, activations read and
-    results written (x fp32, int8 codes + fp32 block scales, fp32 h, fp32
-    y, fp32 out).  u_avg is the mean number of distinct routed experts per
+    results written (x fp32, int8 codes + fp32 block scales, fp32 y, fp32
+    out).  u_avg is the mean number of distinct routed experts per
     step.  Ops count 2 per int8 multiply-add of the expert GEMMs; valu counts
     the per-block dequantization the Q8_32 format requires of them, one
     int32 -> fp32 conversion and one fma per output and 32-block."""

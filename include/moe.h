@@ -200,12 +200,12 @@ int moe_workspace_flags(void *workspace, int32_t *flags, void *stream);
  * caller's arrays (n_stages entries, index = stage id) and forgets them. */
 typedef struct moe_prof moe_prof;
 enum {
-    MOE_STAGE_ROUTE = 0,   /* decode batches: quantize x, router logits, shared-expert gate/up */
+    MOE_STAGE_ROUTE = 0,   /* decode batches: quantize x, router logits */
     MOE_STAGE_QUANT = 1,   /* batched: activation quantizer */
     MOE_STAGE_LOGITS = 2,  /* batched: router logits */
     MOE_STAGE_SELECT = 3,  /* top-k / hash selection (decode batches of 2..32: + sort, work list) */
     MOE_STAGE_SORT = 4,    /* batched: token sort into per-expert work lists */
-    MOE_STAGE_GATEUP = 5,  /* expert gate/up + SwiGLU + quantize h (one token: + selection, work list) */
+    MOE_STAGE_GATEUP = 5,  /* routed and shared gate/up + SwiGLU + quantize h (one token: + selection, work list) */
     MOE_STAGE_DOWN = 6,    /* expert down projection (one token: + the weighted combine) */
     MOE_STAGE_COMBINE = 7, /* sum over each token's experts (ascending id) + shared */
     MOE_N_STAGES = 8

@@ -200,8 +200,8 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
     return (int)r;
 }
 
-// One 32-block of fp32 values held in registers (loaded apart from the
-// quantization so a kernel can request it before a long weight stream).
+// One 32-block of fp32 values held in registers, then quantized: codes,
+// scale and (for Q2 experts) the two 16-subblock code sums.
 struct QBlock {
     float v[32];
     __device__ __forceinline__ void load(const float *__restrict__ x, int64_t blk) {

@@ -195,9 +195,8 @@ __global__ __launch_bounds__(256) void decode_select_kernel(LayerArgs a) {
 // a kernel of its own (it costs each workgroup about as much as its first
 // weight request, and saves a dependent launch).  blockIdx.y is the slot: the
 // position of the workgroup's expert among the distinct selected experts in
-// ascending id; the slot after the last routed one is the shared expert,
-// whose gate/up rows stream from the start (the front kernel computes only
-// the router for one token).  Workgroup (0, 0) publishes the routing for the down
+// ascending id; the slots after the last routed one are the shared expert's,
+// whose gate/up rows stream from the start.  Workgroup (0, 0) publishes the routing for the down
 // kernel and the debug copies: ids and w in rank order, perm (pairs by
 // expert, then slot), counts, offsets and the work list.
 struct Sel1Smem {

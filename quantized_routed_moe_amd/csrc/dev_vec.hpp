@@ -176,14 +176,6 @@ __device__ __forceinline__ void subblock_sums(VecSmem<K, NTOK> &sm, int cnt) {
 
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// Rows per workgroup of the gate/up kernels that leave h unquantized: at least
-// 8 (small workgroups spread a 2048-row matrix over 256 of them) and a whole
-// wave pass of each of the 4 waves.
-template <int K, int FMT>
-struct GuRows {
-    static constexpr int v = 4 * Geo<K, FMT>::RPW > 8 ? 4 * Geo<K, FMT>::RPW : 8;
-};
-
 // Ring depth of gate/up rows (row passes held by a wave): the current pass
 // and the next two in flight.  (Six for the small 2-bit rows measured
 // slower: the one-token 2-bit gate/up is not bound by rows in flight.)
