@@ -128,8 +128,10 @@ __device__ __forceinline__ float lane_dot(const RowRegs<K, kFmtQ2, LPR> &w, cons
         P = sdot4((int)((wv >> 4) & 0x03030303u), x.z, P);
         P = sdot4((int)((wv >> 6) & 0x03030303u), x.w, P);
         const int s = (int)((w.sm >> (8 * jj)) & 15u), m = (int)((w.sm >> (8 * jj + 4)) & 15u);
-        SP[jj >> 1] += s * P;
-        SM[jj >> 1] += m * as16[4 * seg + jj];
+        // 24-bit multiplies (full rate): s, m < 16, |P| <= 16*3*127 and
+        // |as16| <= 16*127, so every product is exact in 24 bits
+        SP[jj >> 1] += __mul24(s, P);
+        SM[jj >> 1] += __mul24(m, as16[4 * seg + jj]);
         if (dump) dump[4 * seg + jj] = P;
     }
     // explicit roundings: the same value in every kernel that inlines this
