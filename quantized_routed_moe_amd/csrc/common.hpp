@@ -143,6 +143,13 @@ __device__ __forceinline__ float bfly_step(float v, Op op) {
 }
 
 template <int D, class Op>
+__device__ __forceinline__ uint32_t bfly_step(uint32_t v, Op op) {
+    uint32_t a, b;
+    bfly_pair_u32<D>(v, a, b);
+    return op(a, b);
+}
+
+template <int D, class Op>
 __device__ __forceinline__ double bfly_step(double v, Op op) {
     const uint64_t u = (uint64_t)__double_as_longlong(v);
     uint32_t la, lb, ha, hb;

@@ -88,29 +88,16 @@ __device__ __forceinline__ uint32_t key_order(float key) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Maximum of v over the wave, returned uniform: a prefix maximum inside each
-// 16-lane row (DPP row shifts by 1, 2, 4, 8; a lane without a source keeps 0),
-// then the maxima of the four rows' last lanes.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
-    return max(max(r0, r1), max(r2, r3));
-}
-
 // One wave selects the top-k (k <= 8 <= E) experts of one token from its keys
 // (larger key first, equal keys: smaller expert id) and weights them by
-// score / sum of the selected scores, summed in rank order.  k rounds: the
-// wave maximum of the remaining key images, the smallest expert id holding
-// it (one ballot per candidate slot, slots in id order), which is then
-// removed.  Lane `rank` keeps the id and score of that rank; lanes 0..k-1
-// write the result.
-//  PER candidate slots per lane (64 * PER >= E); slots past E hold 0, below
-//  every key image, and are never taken.
-// The token's keys (as order-preserving images) and scores, PER per lane.
+// score / sum of the selected scores, summed in rank order.  k rounds, each
+// on the vector ALUs without branches: the wave maximum m of the remaining
+// key images (xor butterfly), the smallest expert id holding m (a per-lane
+// minimum over its candidate slots, then a butterfly minimum), whose slot is
+// then cleared; its score is read from the owning lane.  Lane `rank` keeps
+// the id and score of that rank; lanes 0..k-1 write the result.
+//  PER candidate slots per lane (64 * PER >= E), expert id lane + 64*slot;
+//  slots past E hold 0, below every key image, and are never taken.
 template <int PER>
 struct KeyRegs {
     uint32_t u[PER];
@@ -129,35 +116,30 @@ struct KeyRegs {
 
 template <int PER>
 __device__ void select_keys_from(KeyRegs<PER> r, int k, int &my_id, float &my_w, int lane) {
-    uint32_t *u = r.u;
-    const float *s = r.s;
+    auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    auto umin = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
     my_id = 0;
     float my_s = 0.0f, S = 0.0f;
-    for (int r = 0; r < k; ++r) {
-        uint32_t lm = u[0];
+    for (int rank = 0; rank < k; ++rank) {
+        uint32_t lm = r.u[0];
 #pragma unroll
-        for (int i = 1; i < PER; ++i) lm = max(lm, u[i]);
-        const uint32_t m = wave_max_u32(lm);
-        // smallest id holding m: the first slot (ids lane + 64*i) with a match, its lowest lane
-        int slot = -1, owner = 0;
+        for (int i = 1; i < PER; ++i) lm = umax(lm, r.u[i]);
+        const uint32_t m = group_reduce<64>(lm, umax);
+        uint32_t cid = 0xffffffffu;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) cid = umin(cid, r.u[i] == m ? (uint32_t)(lane + 64 * i) : 0xffffffffu);
+        const uint32_t id = group_reduce<64>(cid, umin);  // the same in every lane
+        float sl = 0.0f;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const uint64_t b = __ballot(u[i] == m);
-            if (slot < 0 && b != 0ull) {
-                slot = i;
-                owner = __builtin_ctzll(b);
-            }
+            const bool hit = (uint32_t)(lane + 64 * i) == id;
+            sl = hit ? r.s[i] : sl;
+            r.u[i] = hit ? 0u : r.u[i];
         }
-        float sx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (i == slot) {
-                sx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[i]), owner));
-                if (lane == owner) u[i] = 0u;
-            }
+        const float sx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sl), (int)(id & 63u)));
         S += sx;
-        if (lane == r) {
-            my_id = owner + 64 * slot;
+        if (lane == rank) {
+            my_id = (int)id;
             my_s = sx;
         }
     }
