@@ -37,9 +37,8 @@ namespace qrmoe {
 
 constexpr int kTM = 64;                  // pairs per tile
 constexpr int kTN = 64;                  // columns per tile
-// K chunk staged per step (KC blocks): gate/up 4 (its registers are full),
-// down 8 (twice the compute between a chunk's request and its use).
-constexpr int kKCGateUp = 4;
+// K chunk staged per step of the down GEMM: 8 blocks (twice the compute
+// between a chunk's request and its use).
 constexpr int kKCDown = 8;
 template <int KC>
 constexpr int row_bytes() { return KC * 32 + 16; }  // padded LDS row (bytes)
@@ -179,60 +178,134 @@ __device__ __forceinline__ float wscale(const Smem &sm, int r, int kb) {
     return f16_to_f32((uint16_t)((kb & 1) ? (v >> 16) : (v & 0xffff)));
 }
 
+// ------------------------------------------- direct global -> LDS staging
+// buffer_load_dword{,x4} ... lds writes lane l's 4 (16) bytes to LDS at
+// base + 4l (16l): one wave fills 256 B (1 KB) of LDS with no VGPRs and no
+// ds_write.  The loads go through a buffer descriptor whose record count is
+// the source tensor's size, so an offset past it reads zeros instead of
+// touching other memory.  A wave waits for its own loads of a chunk with an
+// explicit vmcnt count, then a barrier makes every wave's loads visible.
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    // raw byte buffer: stride 0, range check against `bytes`, 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, (int)voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, (int)voff, 0, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ------------------------------------------------------------- gate / up
+// One workgroup: 64 pairs x 64 columns of gate and of up (128 weight rows),
+// 8 waves, (gate | up) x 2 (pairs) x 2 (columns), each wave one 32 x 32 tile
+// of one matrix.  K runs in chunks of 4 blocks through a 3-stage LDS ring:
+// chunk c+2 streams in while chunk c is computed, one barrier per chunk.
+// A row holds a chunk's 128 code bytes as 8 16-byte slots, slot q of row r
+// holding piece q ^ (r & 7), so the MFMA operand reads (8 consecutive rows
+// at one piece) fall on 8 different bank groups.
+constexpr int kGuKC = 4;       // blocks per chunk
+constexpr int kGuStages = 3;   // LDS ring depth
+constexpr int kGuRow = kGuKC * 32;
+struct GuStage {
+    int8_t A[kTM * kGuRow];        // activation codes of the chunk (swizzled rows)
+    int8_t B[2 * kTN * kGuRow];    // gate rows 0..63, up rows 64..127 (swizzled)
+    float sa[kTM * kGuKC];         // activation block scales [pair][block]
+    uint16_t sw[2 * kTN * kGuKC];  // weight block scales [row][block], fp16
+};
+struct GuSmem {
+    GuStage st[kGuStages];
+    int32_t arow[kTM];
+    int32_t pair[kTM];
+    float w[kTM];
+};
+static_assert(sizeof(GuStage) % 16 == 0, "stage alignment");
+static_assert(kTM * kTN * 4 <= (int)sizeof(GuStage), "SwiGLU exchange fits in one stage");
+
 template <int H, bool DUMP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gateup_mfma_kernel(LayerArgs a) {
-    constexpr int NT = 512, kKC = kKCGateUp, NB = H / 32, NC = NB / kKC, NBR = 2 * kTN;
-    static_assert(NC >= 1 && NB % kKC == 0, "K chunks");
-    __shared__ GemmSmem<NBR, kKC> sm;
+    constexpr int NB = H / 32, NC = NB / kGuKC;
+    static_assert(NC >= 2 && NB % kGuKC == 0, "K chunks");
+    __shared__ __attribute__((aligned(16))) GuSmem sm;
     const int g = blockIdx.y;
     if (g >= a.ws.ctl[kCtlGroups]) return;
     const int4 grp = a.ws.groups[g];
     const bool shared = grp.x == a.d.E;
     const Dims &d = a.d;
     setup_tile(a, sm, grp, shared, false);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, n = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, n = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int which = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;  // which: 0 gate, 1 up
     const uint8_t *gmat = shared ? a.wt.sh_gate : a.wt.gate + grp.x * q8_bytes(d.F, H);
     const uint8_t *umat = shared ? a.wt.sh_up : a.wt.up + grp.x * q8_bytes(d.F, H);
     const int c0 = blockIdx.x * kTN;
-    auto brow = [&](int j) {
-        return j < kTN ? std::make_pair(gmat, c0 + j) : std::make_pair(umat, c0 + j - kTN);
+    const uint32_t mat_bytes = (uint32_t)q8_bytes(d.F, H);
+
+    // ---- this wave's four loads per chunk (byte offsets at chunk 0)
+    const __amdgpu_buffer_rsrc_t r_xq = buf_rsrc(a.ws.xq, (uint32_t)((int64_t)d.T * H));
+    const __amdgpu_buffer_rsrc_t r_gate = buf_rsrc(gmat, mat_bytes), r_up = buf_rsrc(umat, mat_bytes);
+    const int lrow = 8 * wave + (lane >> 3), piece = (lane & 7) ^ (lane >> 3);
+    const uint32_t off_a = (uint32_t)sm.arow[lrow] * H + 16 * piece;          // activation row lrow
+    const uint32_t off_w = (uint32_t)(c0 + lrow) * H + 16 * piece;            // gate / up row lrow
+    __amdgpu_buffer_rsrc_t r_s;
+    uint32_t off_s;
+    if (wave < 4) {  // activation scales: pairs 16 wave .. +15, 4 blocks each
+        r_s = buf_rsrc(a.ws.xd, (uint32_t)((int64_t)d.T * (H / 32) * 4));
+        off_s = ((uint32_t)sm.arow[16 * wave + (lane >> 2)] * (H / 32) + (lane & 3)) * 4;
+    } else {         // weight scales: rows 32 (wave-4) .. +31 of B, two dwords (4 fp16) each
+        const int row = 32 * (wave - 4) + (lane >> 1);
+        r_s = wave < 6 ? r_gate : r_up;
+        off_s = (uint32_t)d.F * H + (uint32_t)(c0 + (row & (kTN - 1))) * (H / 32) * 2 + 4 * (lane & 1);
+    }
+    auto issue = [&](int c, int stg) {
+        GuStage &S = sm.st[stg];
+        dma16(r_xq, &S.A[wave * 1024], off_a + c * kGuRow);
+        dma16(r_gate, &S.B[wave * 1024], off_w + c * kGuRow);
+        dma16(r_up, &S.B[kTN * kGuRow + wave * 1024], off_w + c * kGuRow);
+        if (wave < 4) dma4(r_s, &S.sa[wave * 64], off_s + c * (kGuKC * 4));
+        else dma4(r_s, &S.sw[(wave - 4) * 128], off_s + c * (kGuKC * 2));
     };
+
+    // ---- this lane's LDS reads: operand rows and the swizzled slot of each block half
+    const int am = wm * 32 + n, bj = which * kTN + wn * 32 + n;
+    uint32_t slot[kGuKC];
+#pragma unroll
+    for (int kb = 0; kb < kGuKC; ++kb) slot[kb] = 16 * ((2 * kb + half) ^ (n & 7));
     const int col = c0 + wn * 32 + n;  // this lane's h column (gate/up row)
-    const int brow_lds = which * kTN + wn * 32 + n;
+    const bool live = wm * 32 < grp.z;  // this wave's 32 pairs hold at least one real pair
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    Stage<NT, NBR, kKC> st;
-    st.template setup<H>(sm, a.ws.xq, a.ws.xd, d.F, brow);
-    st.load(0);
-#pragma unroll 1
-    for (int c = 0; c < NC; ++c) {
-        __syncthreads();
-        st.store(sm);
-        __syncthreads();
-        if (c + 1 < NC) st.load(c + 1);
-        // block kb's int8 MFMA is issued before block kb-1's conversions and fmas
+
+    issue(0, 0);
+    issue(1, 1);
+    auto compute = [&](int c, const GuStage &S) {
         auto block_mfma = [&](int kb) {
-            const i32x4 av = *reinterpret_cast<const i32x4 *>(&sm.A[wm * 32 + n][kb * 32 + 16 * half]);
-            const i32x4 bv = *reinterpret_cast<const i32x4 *>(&sm.B[brow_lds][kb * 32 + 16 * half]);
+            const i32x4 av = *reinterpret_cast<const i32x4 *>(&S.A[am * kGuRow + slot[kb]]);
+            const i32x4 bv = *reinterpret_cast<const i32x4 *>(&S.B[bj * kGuRow + slot[kb]]);
             const v16i zero = {};
             return __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, zero, 0, 0, 0);
         };
         v16i cnext = block_mfma(0);
 #pragma unroll
-        for (int kb = 0; kb < kKC; kb += 2) {
+        for (int kb = 0; kb < kGuKC; kb += 2) {
             // scale products of blocks kb (registers 0..15) and kb+1 (16..31)
-            const float dx = sm.sa[kb + half][wm * 32 + n];
-            const float dw = wscale(sm, brow_lds, kb + half);
+            const float dx = S.sa[am * kGuKC + kb + half];
+            const float dw = f16_to_f32(S.sw[bj * kGuKC + kb + half]);
             const v32f pz = {};
             const v32f ps = __builtin_amdgcn_mfma_f32_32x32x1f32(dx, dw, pz, 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int b = c * kKC + kb + j;
+                const int b = c * kGuKC + kb + j;
                 const v16i cv = cnext;
-                if (kb + j + 1 < kKC) cnext = block_mfma(kb + j + 1);
+                if (kb + j + 1 < kGuKC) cnext = block_mfma(kb + j + 1);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[i] = __fmaf_rn((float)cv[i], ps[16 * j + i], acc[i]);
                 if (DUMP && (col % a.dump.stride == 0)) {
@@ -247,18 +320,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
                 }
             }
         }
+    };
+    // chunk c: wait for this wave's loads of c (those of c+1 may still fly),
+    // barrier (every wave's loads of c landed, every wave done with c-1),
+    // refill the stage of c-1 with c+2, compute c.
+    auto step = [&](int c, auto stg_c) {
+        constexpr int stg = decltype(stg_c)::value;
+        if (c + 1 < NC) wait_vm<4>();
+        else wait_vm<0>();
+        lds_barrier();
+        if (c + 2 < NC) issue(c + 2, (stg + 2) % kGuStages);
+        if (live) compute(c, sm.st[stg]);
+    };
+#pragma unroll 1
+    for (int c = 0; c < NC; c += kGuStages) {
+        step(c, std::integral_constant<int, 0>{});
+        if (c + 1 < NC) step(c + 1, std::integral_constant<int, 1>{});
+        if (c + 2 < NC) step(c + 2, std::integral_constant<int, 2>{});
     }
-    // the up waves hand their sums to the gate waves through LDS (the staged
-    // weights are no longer needed): SwiGLU, then quantize each pair's 32
-    // columns (the 32 lanes of a half-wave)
+    // the up waves hand their sums to the gate waves through LDS (the ring is
+    // drained: the last chunk waited for every load): SwiGLU, then quantize
+    // each pair's 32 columns (the 32 lanes of a half-wave)
     __syncthreads();
-    float *hx = reinterpret_cast<float *>(&sm.B[0][0]);  // [64 pairs][64 columns]
+    float *hx = reinterpret_cast<float *>(&sm.st[0]);  // [64 pairs][64 columns]
     if (which == 1) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) hx[(wm * 32 + acc_row(i, lane)) * kTN + wn * 32 + n] = acc[i];
     }
     __syncthreads();
-    if (which == 0) {
+    if (which == 0 && live) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int m = wm * 32 + acc_row(i, lane);
