@@ -21,9 +21,8 @@
 // wave one 32 x 32 block of it: (B rows 0..63 | 64..127) x 2 (pairs) x
 // 2 (rows).
 //  gate/up  B rows 0..63 are 64 gate rows, 64..127 the same 64 up rows; after
-//           K, the up waves pass their sums through LDS and the gate waves
-//           apply SwiGLU and the per-32-column quantization of h (a wave's
-//           32 columns = one block).
+//           K, all sums pass through LDS and every wave applies SwiGLU and
+//           the per-32-column quantization of h to 8 pairs.
 //  down     B rows are 128 consecutive rows of the down matrix; y = w_pair *
 //           acc, combined afterwards in ascending expert id by the combine
 //           kernel.
@@ -87,7 +86,7 @@ struct RingSmem {
     float w[kTM];
 };
 static_assert(sizeof(RingStage) % 16 == 0, "stage alignment");
-static_assert(kTM * (kTB / 2) * 4 <= (int)sizeof(RingStage), "SwiGLU exchange fits in one stage");
+static_assert(2 * kTM * (kTB / 2) * 4 <= kStages * (int)sizeof(RingStage), "SwiGLU exchange fits in the ring");
 
 // Tile setup: pairs, activation rows and combine weights of the tile's rows.
 __device__ __forceinline__ void setup_tile(const LayerArgs &a, RingSmem &sm, int4 grp, bool shared, bool act_is_h) {
@@ -226,30 +225,40 @@ __device__ __forceinline__ void expert_gemm(const LayerArgs &a, RingSmem &sm) {
         if (c + 2 < NC) step(c + 2, std::integral_constant<int, 2>{});
     }
     if constexpr (GU) {
-        // the up waves hand their sums to the gate waves through LDS (the
-        // ring is drained: the last chunk waited for every load): SwiGLU,
-        // then quantize each pair's 32 columns (the 32 lanes of a half-wave)
+        // SwiGLU and the per-32-column quantization of h, spread over all
+        // waves: every wave parks its sums in LDS (the ring is drained: the
+        // last chunk waited for every load), then lane l of wave w takes pair
+        // 8w + l/8 and its 8 columns 8(l%8) .. +7; the 4 lanes of one 32-column
+        // block share its scale.
         __syncthreads();
-        float *hx = reinterpret_cast<float *>(&sm.st[0]);  // [64 pairs][64 columns]
-        if (which == 1) {
+        float *gx = reinterpret_cast<float *>(&sm.st[0]);  // [64 pairs][64 columns] gate, then up
 #pragma unroll
-            for (int i = 0; i < 16; ++i) hx[(wm * 32 + acc_row(i, lane)) * (kTB / 2) + wn * 32 + n] = acc[i];
+        for (int i = 0; i < 16; ++i)
+            gx[which * kTM * (kTB / 2) + (wm * 32 + acc_row(i, lane)) * (kTB / 2) + wn * 32 + n] = acc[i];
+        __syncthreads();
+        const int m = 8 * wave + (lane >> 3), cg = lane & 7;
+        const float *grow = gx + m * (kTB / 2) + 8 * cg, *urow = grow + kTM * (kTB / 2);
+        const float4 g0 = *reinterpret_cast<const float4 *>(grow), g1 = *reinterpret_cast<const float4 *>(grow + 4);
+        const float4 u0 = *reinterpret_cast<const float4 *>(urow), u1 = *reinterpret_cast<const float4 *>(urow + 4);
+        const float hv[8] = {swiglu(g0.x, u0.x), swiglu(g0.y, u0.y), swiglu(g0.z, u0.z), swiglu(g0.w, u0.w),
+                             swiglu(g1.x, u1.x), swiglu(g1.y, u1.y), swiglu(g1.z, u1.z), swiglu(g1.w, u1.w)};
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(hv[j]));
+        amax = group_max<4>(amax);
+        const float dsc = quant_scale(amax);
+        const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
+        uint32_t q0 = 0, q1 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            q0 |= ((uint32_t)quant_code(hv[j], inv) & 0xffu) << (8 * j);
+            q1 |= ((uint32_t)quant_code(hv[4 + j], inv) & 0xffu) << (8 * j);
         }
-        __syncthreads();
-        if (which == 0 && live) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = wm * 32 + acc_row(i, lane);
-                const float hv = swiglu(acc[i], hx[m * (kTB / 2) + wn * 32 + n]);
-                const float amax = group_max<32>(fabsf(hv));
-                const float dsc = quant_scale(amax);
-                const float inv = dsc > 0.0f ? 1.0f / dsc : 0.0f;
-                if (m < grp.z) {
-                    const int64_t p = sm.pair[m];
-                    a.ws.hq[p * d.F + col] = (int8_t)quant_code(hv, inv);
-                    if (n == 0) a.ws.hd[p * (d.F / 32) + col / 32] = dsc;
-                }
-            }
+        if (m < grp.z) {
+            const int64_t p = sm.pair[m];
+            const int hc = r0 + 8 * cg;  // first h column of this lane
+            *reinterpret_cast<uint2 *>(&a.ws.hq[p * d.F + hc]) = make_uint2(q0, q1);
+            if ((cg & 3) == 0) a.ws.hd[p * (d.F / 32) + hc / 32] = dsc;
         }
     } else if (live) {
 #pragma unroll
