@@ -48,31 +48,6 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-// ------------------------------------------- direct global -> LDS staging
-// buffer_load_dword{,x4} ... lds writes lane l's 4 (16) bytes to LDS at
-// base + 4l (16l): one wave fills 256 B (1 KB) of LDS with no VGPRs and no
-// ds_write.  The loads go through a buffer descriptor whose record count is
-// the source tensor's size, so an offset past it reads zeros instead of
-// touching other memory.  A wave waits for its own loads of a chunk with an
-// explicit vmcnt count, then a barrier makes every wave's loads visible.
-typedef __attribute__((address_space(3))) void *lds_ptr;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
-    // raw byte buffer: stride 0, range check against `bytes`, 32-bit data format
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, (int)voff, 0, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, (int)voff, 0, 0, 0);
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 struct RingStage {
     int8_t A[kTM * kRow];      // activation codes of the chunk (swizzled rows)
     int8_t B[kTB * kRow];      // weight codes of the chunk (swizzled rows)
