@@ -310,6 +310,28 @@ def test_out_of_range_token_id_is_flagged_one_token():
     assert layer.flags() & 1
 
 
+def test_mfma_tile_boundaries():
+    """Hash routing, top-1, with a table that gives experts exactly 1, 31, 32,
+    33, 63, 64, 65 and 129 tokens (the others none), in shuffled token order:
+    every shape of the MFMA GEMMs' 64-pair tiles (one or both 32-pair halves
+    live, ragged, several tiles per expert, empty experts between them) and the
+    shared expert's ragged last tile, against the oracle with exact block sums."""
+    qr = _qr()
+    counts = [1, 31, 32, 33, 63, 64, 65, 129]
+    T = sum(counts)
+    cfg = ms.LayerConfig("q8_mfma_tile_edges", 512, 16, 1, 256, T, route="hash", vocab=T, seed=63)
+    inp = ms.make_inputs(cfg)
+    order = np.random.default_rng(63).permutation(T).astype(np.int32)
+    experts = np.repeat(2 * np.arange(len(counts)), counts).astype(np.int32)
+    inp["hash_table"] = np.empty((T, 1), dtype=np.int32)
+    inp["hash_table"][order, 0] = experts
+    inp["token_ids"] = np.arange(T, dtype=np.int32)
+    layer = qr.MoELayer(512, 16, 1, 256, True, "q8", "hash", T).load(inp)
+    g = run_gpu(cfg, inp, layer, stride=8)
+    assert np.array_equal(g["counts"][::2][:len(counts)], counts)
+    check(cfg, inp, g, rows=np.arange(0, T, 3), stride=8)
+
+
 def test_repeated_expert_in_an_unchecked_hash_row():
     """A table row naming one expert twice (rejected by the table check, used
     anyway): one-token calls and a batched call agree bit for bit, and the
