@@ -110,7 +110,7 @@ def source_hash(kernel):
 
 def stage_kernel(cfg, stage):
     """Name of the one kernel a stage launches on this workload's path."""
-    T, mfma = cfg.tokens, (cfg.routed_fmt == "q8" and cfg.hidden >= 256 and cfg.ffn >= 256)
+    T, mfma = cfg.tokens, (cfg.hidden >= 256 and cfg.ffn >= 256)
     if T <= 32:
         return {"route": "decode_front_kernel", "select": "decode_select_kernel",
                 "gateup": "decode_gateup1_kernel" if T == 1 else "gateup_vec_kernel",

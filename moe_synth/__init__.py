@@ -174,6 +174,10 @@ CONFIGS = {
     "decode_topk4": LayerConfig("decode_topk4", 4096, 256, 4, 2048, 1, seed=1),
     "hash_scored_decode": LayerConfig("hash_scored_decode", 4096, 256, 6, 2048, 32, route="hash_scored", seed=3),
     "decode_motif3": LayerConfig("decode_motif3", 4096, 384, 8, 2048, 1, seed=5),
+    # The prefill chunk with 2-bit routed experts (shared expert Q8), the
+    # weight families the pages' model runs prefill with ("DwarfStar (ds4) —
+    # ROCm / gfx1151 fork", Model Weights).
+    "prefill_q2": LayerConfig("prefill_q2", 4096, 256, 6, 2048, 2048, routed_fmt="q2", seed=6),
 }
 
 

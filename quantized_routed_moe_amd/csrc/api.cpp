@@ -57,7 +57,7 @@ int64_t max_groups(const moe_shape *s, int64_t T, int64_t G) {
 }
 
 struct Layout {
-    size_t ctl, logits, scores, keys, ids, w, xq, xd, xs16, counts, offsets, perm, groups, hq, hd, y, total;
+    size_t ctl, logits, scores, keys, ids, w, xq, xd, xs16, counts, offsets, perm, groups, hq, hd, hs16, y, total;
 };
 
 
@@ -90,6 +90,8 @@ Layout make_layout(const moe_shape *s, int64_t T) {
     L.groups = take(G * 16);
     L.hq = take(P * F);
     L.hd = take(P * (F / 32) * 4);
+    // the 2-bit down GEMM of batches past the decode sizes reads h's subblock sums
+    L.hs16 = take(s->routed_fmt == MOE_FMT_Q2_256 && T > kDecodeMaxT ? P * (F / 16) * 4 : 0);
     L.y = take(P * H * 4);
     L.total = o;
     return L;
@@ -189,7 +191,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
               (int32_t *)(base + L.xs16), (int32_t *)(base + L.counts), (int32_t *)(base + L.offsets),
               (int32_t *)(base + L.perm), (int4 *)(base + L.groups), (int8_t *)(base + L.hq),
               (float *)(base + L.hd), (float *)(base + L.y), (float *)(base + L.scores),
-              (float *)(base + L.keys)};
+              (float *)(base + L.keys), (int32_t *)(base + L.hs16)};
     const bool dump = dbg && (dbg->gate_sums || dbg->up_sums || dbg->down_sums);
     const bool q2 = shape->routed_fmt == MOE_FMT_Q2_256;
     a.dump = Dump{dump ? dbg->gate_sums : nullptr, dump ? dbg->up_sums : nullptr, dump ? dbg->down_sums : nullptr,
@@ -218,9 +220,9 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
             run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
         }
     } else {
-        // Q8 experts go through the grouped int8 MFMA GEMMs (64-pair tiles);
-        // 2-bit experts and the smallest shapes stay on the VALU kernels.
-        const bool mfma = shape->routed_fmt == MOE_FMT_Q8_32 && H >= 256 && shape->ffn >= 256;
+        // Q8 and 2-bit experts go through the grouped int8 MFMA GEMMs (64-pair
+        // tiles); the smallest shapes stay on the VALU kernels.
+        const bool mfma = H >= 256 && shape->ffn >= 256;
         const int64_t tiles = mfma ? max_groups(shape, T, kMfmaTile) : mg;
         a.group_tok = mfma ? kMfmaTile : kVecTok;
         run(MOE_STAGE_QUANT, [&] { return launch_quant(a, s); });

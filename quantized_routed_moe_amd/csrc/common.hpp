@@ -67,6 +67,7 @@ struct Ws {
     float *y;        // [P][H] weighted expert outputs (w already applied)
     float *scores;   // [T][E] sigmoid scores
     float *keys;     // [T][E] selection keys (score + bias)
+    int32_t *hs16;   // [P][F/16] sums of hq over 16-subblocks (2-bit down GEMM; batched path only)
 };
 
 struct Weights {

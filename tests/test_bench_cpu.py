@@ -44,10 +44,11 @@ def test_stage_kernels_follow_the_dispatch(bench):
     assert bench.stage_kernel(c["hash_decode"], "gateup") == "gateup_vec_kernel"
     assert bench.stage_kernel(c["prefill"], "gateup") == "gateup_mfma_kernel"
     assert bench.stage_kernel(c["prefill"], "down") == "down_mfma_kernel"
+    assert bench.stage_kernel(c["prefill_q2"], "gateup") == "gateup_mfma_kernel"
     # 2048 tokens x top-6 = 12,288 pairs: the chunked sort
     assert bench.stage_kernel(c["prefill"], "sort") == "sort_scatter_kernel"
     every = set(bench.KERNEL_SOURCES)
-    for name in ("decode_q8", "decode_q2", "hash_decode", "prefill"):
+    for name in ("decode_q8", "decode_q2", "hash_decode", "prefill", "prefill_q2"):
         for stage in ("route", "quant", "logits", "select", "sort", "gateup", "down", "combine"):
             k = bench.stage_kernel(c[name], stage)
             assert k is None or k in every, (name, stage, k)

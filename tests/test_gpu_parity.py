@@ -158,6 +158,10 @@ SMALL = [
     ms.LayerConfig("q8_mfma_1024_T300", 1024, 16, 4, 512, 300, seed=26),
     ms.LayerConfig("q8_mfma_hash_T77", 512, 64, 6, 256, 77, route="hash", vocab=5000, seed=27),
     ms.LayerConfig("q8_mfma_noshared_T45", 256, 8, 3, 256, 45, shared=False, seed=28),
+    # 2-bit routed experts on the MFMA GEMMs (the shared expert Q8 in the same launches)
+    ms.LayerConfig("q2_mfma_512_T300", 512, 16, 4, 512, 300, routed_fmt="q2", seed=64),
+    ms.LayerConfig("q2_mfma_hash_T77", 1024, 64, 6, 512, 77, routed_fmt="q2", route="hash", vocab=5000, seed=65),
+    ms.LayerConfig("q2_mfma_noshared_T45", 512, 8, 3, 1024, 45, routed_fmt="q2", shared=False, seed=66),
     # routing variants: score-weighted hash, hash rows wider than top-k, 384 experts top-8
     ms.LayerConfig("q8_hashscored_T1", 512, 32, 6, 256, 1, route="hash_scored", vocab=300, seed=50),
     ms.LayerConfig("q8_hashscored_reduced_T9", 512, 32, 4, 256, 9, route="hash_scored", vocab=300, table_k=6,
@@ -271,9 +275,12 @@ def test_empty_batch_is_a_no_op():
                                  ms.LayerConfig("batch_learned_T3", 1024, 64, 6, 512, 3, seed=36),
                                  ms.LayerConfig("batch_hash", 512, 32, 4, 256, 12, route="hash", vocab=300,
                                                 seed=32),
-                                 ms.LayerConfig("batch_q2_T40", 512, 32, 4, 512, 40, routed_fmt="q2", seed=35)],
+                                 ms.LayerConfig("batch_q2_T32", 512, 32, 4, 512, 32, routed_fmt="q2", seed=35)],
                          ids=lambda c: c.name)
 def test_batched_equals_single_token_calls_bitwise(cfg):
+    """Batches the VALU expert kernels serve (up to 32 tokens) give every token
+    the bits of a one-token call.  (Longer batches run the MFMA GEMMs, which
+    accumulate in another order; they are held to the oracle tolerance.)"""
     inp, layer = case(cfg)
     x = torch.from_numpy(inp["x"]).cuda()
     tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route != "learned" else None
@@ -310,23 +317,27 @@ def test_out_of_range_token_id_is_flagged_one_token():
     assert layer.flags() & 1
 
 
-def test_mfma_tile_boundaries():
+@pytest.mark.parametrize("fmt", ["q8", "q2"])
+def test_mfma_tile_boundaries(fmt):
     """Hash routing, top-1, with a table that gives experts exactly 1, 31, 32,
     33, 63, 64, 65 and 129 tokens (the others none), in shuffled token order:
     every shape of the MFMA GEMMs' 64-pair tiles (one or both 32-pair halves
     live, ragged, several tiles per expert, empty experts between them) and the
-    shared expert's ragged last tile, against the oracle with exact block sums."""
+    shared expert's ragged last tile, against the oracle with exact block sums
+    (Q8 blocks, or 2-bit subblocks)."""
     qr = _qr()
     counts = [1, 31, 32, 33, 63, 64, 65, 129]
     T = sum(counts)
-    cfg = ms.LayerConfig("q8_mfma_tile_edges", 512, 16, 1, 256, T, route="hash", vocab=T, seed=63)
+    F = 256 if fmt == "q8" else 512
+    cfg = ms.LayerConfig(f"{fmt}_mfma_tile_edges", 512, 16, 1, F, T, routed_fmt=fmt, route="hash", vocab=T,
+                         seed=63)
     inp = ms.make_inputs(cfg)
     order = np.random.default_rng(63).permutation(T).astype(np.int32)
     experts = np.repeat(2 * np.arange(len(counts)), counts).astype(np.int32)
     inp["hash_table"] = np.empty((T, 1), dtype=np.int32)
     inp["hash_table"][order, 0] = experts
     inp["token_ids"] = np.arange(T, dtype=np.int32)
-    layer = qr.MoELayer(512, 16, 1, 256, True, "q8", "hash", T).load(inp)
+    layer = qr.MoELayer(512, 16, 1, F, True, fmt, "hash", T).load(inp)
     g = run_gpu(cfg, inp, layer, stride=8)
     assert np.array_equal(g["counts"][::2][:len(counts)], counts)
     check(cfg, inp, g, rows=np.arange(0, T, 3), stride=8)
@@ -393,6 +404,20 @@ def test_full_size_prefill_sampled(T):
     g = run_gpu(cfg, inp, layer, x=x, stride=128)
     rows = np.r_[0, 1, 2, T // 4, T // 2, T - 2, T - 1, np.arange(37, T, T // 12)]
     check(cfg, inp, g, x=x, rows=np.unique(rows), stride=128, name=f"prefill_T{T}")
+    assert np.count_nonzero(g["counts"]) > 0
+
+
+@pytest.mark.slow
+def test_full_size_prefill_q2_sampled():
+    """The 2048-token prefill chunk with 2-bit routed experts (Q8 shared expert)
+    on the MFMA GEMMs: routing, x quantization and the sort bit-exact, outputs
+    and exact 16-subblock sums of sampled tokens."""
+    cfg = ms.CONFIGS["prefill_q2"]
+    inp, layer = case(cfg)
+    T = cfg.tokens
+    g = run_gpu(cfg, inp, layer, stride=128)
+    rows = np.r_[0, 1, 2, T // 4, T // 2, T - 2, T - 1, np.arange(37, T, T // 12)]
+    check(cfg, inp, g, rows=np.unique(rows), stride=128)
     assert np.count_nonzero(g["counts"]) > 0
 
 
