@@ -168,8 +168,12 @@ def stage_model(cfg, qr, u_avg):
             st["logits"] = router + x32 + rout
         st["select"] = (2 * T * E * 4 if has_router else T * 4) + T * k * 8
         st["sort"] = T * k * 4 * 3
-        st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P)
-        st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + P * H * 4
+        # 2-bit experts: the gate/up GEMM reads x's subblock sums and stores
+        # h's, which the down GEMM reads
+        xs16 = T * (H // 16) * 4 if cfg.routed_fmt == "q2" else 0
+        hs16 = Pr * (F // 16) * 4 if cfg.routed_fmt == "q2" else 0
+        st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + xs16 + hq(P) + hs16
+        st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + hs16 + P * H * 4
         st["combine"] = P * H * 4 + x32
     ops = {"gateup": 2 * P * 2 * F * H, "down": 2 * P * H * F}
     valu = {"gateup": 2 * P * 2 * F * (H // 32), "down": 2 * P * H * (F // 32)}
