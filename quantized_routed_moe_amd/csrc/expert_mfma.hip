@@ -380,13 +380,16 @@ __device__ __forceinline__ void expert_gemm_q2(const LayerArgs &a, RingSmem &sm,
         const float4 sav = *reinterpret_cast<const float4 *>(&S.sa[am * kKC]);
         const float sa_k[kKC] = {sav.x, sav.y, sav.z, sav.w};
         const uint2 smw = *reinterpret_cast<const uint2 *>(&S.Bsm[bj * 2]);
-        uint32_t cw[kKC];
-        int32_t xs[kKC];
-#pragma unroll
-        for (int kb = 0; kb < kKC; ++kb) {
-            cw[kb] = S.Bq[bj * 8 + 2 * kb + half];
-            xs[kb] = S.as16[am * 8 + 2 * kb + half];
-        }
+        // a row's 8 code words (and a pair's 8 sums) as two 16-byte reads; this
+        // lane's subblocks are 2kb + half
+        const i32x4 bq0 = *reinterpret_cast<const i32x4 *>(&S.Bq[bj * 8]);
+        const i32x4 bq1 = *reinterpret_cast<const i32x4 *>(&S.Bq[bj * 8 + 4]);
+        const i32x4 xs0 = *reinterpret_cast<const i32x4 *>(&S.as16[am * 8]);
+        const i32x4 xs1 = *reinterpret_cast<const i32x4 *>(&S.as16[am * 8 + 4]);
+        const uint32_t cw[kKC] = {(uint32_t)(half ? bq0.y : bq0.x), (uint32_t)(half ? bq0.w : bq0.z),
+                                  (uint32_t)(half ? bq1.y : bq1.x), (uint32_t)(half ? bq1.w : bq1.z)};
+        const int32_t xs[kKC] = {half ? xs0.y : xs0.x, half ? xs0.w : xs0.z, half ? xs1.y : xs1.x,
+                                 half ? xs1.w : xs1.z};
         // scale/min byte of this lane's subblock 2kb + half
         auto smbyte = [&](int kb) { return ((kb < 2 ? smw.x : smw.y) >> (8 * (2 * (kb & 1)) + 8 * half)) & 0xffu; };
         auto a_op = [&](int kb) { return *reinterpret_cast<const i32x4 *>(&S.A[am * kRow + slot[kb]]); };

@@ -424,7 +424,9 @@ def test_full_size_prefill_q2_sampled():
 # ------------------------------------------------------- graph replay
 @pytest.mark.parametrize("cfg", [ms.LayerConfig("graph_T1", 512, 32, 4, 256, 1, seed=41),
                                  ms.LayerConfig("graph_T7_hash", 512, 32, 4, 256, 7, route="hash", vocab=99, seed=42),
-                                 ms.LayerConfig("graph_T40", 512, 32, 4, 256, 40, seed=43)], ids=lambda c: c.name)
+                                 ms.LayerConfig("graph_T40", 512, 32, 4, 256, 40, seed=43),
+                                 ms.LayerConfig("graph_q2_T70", 512, 32, 4, 512, 70, routed_fmt="q2", seed=44)],
+                         ids=lambda c: c.name)
 def test_graph_replay_matches_eager(cfg):
     """The layer captured in a HIP graph replays to the eager result, replay after replay,
     with eager work and synchronisations in between (nothing in the path is a memset node)."""
