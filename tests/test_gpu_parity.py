@@ -144,6 +144,7 @@ SMALL = [
     ms.LayerConfig("q8_learned_512_T100", 512, 32, 4, 256, 100, seed=14),
     ms.LayerConfig("q2_learned_512", 512, 32, 4, 512, 9, routed_fmt="q2", seed=15),
     ms.LayerConfig("q2_learned_1024_T40", 1024, 24, 3, 512, 40, routed_fmt="q2", seed=16),
+    ms.LayerConfig("q2_learned_512_T33", 512, 32, 4, 512, 33, routed_fmt="q2", seed=68),
     ms.LayerConfig("q8_hash_256", 256, 16, 2, 128, 3, route="hash", vocab=1000, seed=17),
     ms.LayerConfig("q8_hash_256_T50", 256, 16, 2, 128, 50, route="hash", vocab=1000, seed=18),
     ms.LayerConfig("q8_noshared_k1", 256, 8, 1, 256, 5, shared=False, seed=19),
@@ -252,8 +253,12 @@ def test_tied_keys_take_the_smaller_expert_ids(T):
     check(cfg, inp, g, stride=4, name=f"ties_T{T}")
 
 
-def test_max_tokens_small_shape():
-    cfg = ms.LayerConfig("max_tokens", 256, 16, 2, 128, 16384, seed=25)
+@pytest.mark.parametrize("fmt", ["q8", "q2"])
+def test_max_tokens_small_shape(fmt):
+    """The largest batch, 16,384 tokens: Q8 on the VALU kernels (F = 128),
+    2-bit experts on the MFMA GEMMs (H = F = 512)."""
+    cfg = (ms.LayerConfig("max_tokens", 256, 16, 2, 128, 16384, seed=25) if fmt == "q8" else
+           ms.LayerConfig("max_tokens_q2", 512, 16, 2, 512, 16384, routed_fmt="q2", seed=67))
     inp, layer = case(cfg)
     g = run_gpu(cfg, inp, layer, stride=32)
     rows = np.r_[0:3, 8191:8194, 16381:16384]
