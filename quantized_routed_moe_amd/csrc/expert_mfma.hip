@@ -1,9 +1,10 @@
-// Grouped int8 MFMA GEMMs of the expert FFN for batched tokens (Q8_32 and
-// 2-bit Q2_256 weights; the 2-bit body is described at expert_gemm_q2): the token sort gives each expert a list of pairs, cut into tiles
-// of 64 (the expert-tile prefill kernels of "DwarfStar (ds4) — ROCm / gfx1151
-// fork", Performance optimizations, moe_gate_up_mid_expert_tile* /
+// Grouped int8 MFMA GEMMs of the expert FFN for batched tokens, Q8_32 and
+// 2-bit Q2_256 weights (the 2-bit body is described at expert_gemm_q2).  The
+// token sort gives each expert a list of pairs, cut into tiles of 64 (the
+// expert-tile prefill kernels of "DwarfStar (ds4) — ROCm / gfx1151 fork",
+// Performance optimizations, moe_gate_up_mid_expert_tile* /
 // moe_down_expert_tile*; the expert-major schedule of "ds4: dfm Edition",
-// About this fork).  Every 32-element quantization block is one
+// About this fork).  For Q8 weights every 32-element quantization block is one
 // v_mfma_i32_32x32x32_i8 (K = 32 = one block), so the MFMA returns the exact
 // int32 block sum of every (pair, row); those are scaled by the two block
 // scales and accumulated in fp32 in block order.  The scale products
