@@ -110,7 +110,9 @@ def source_hash(kernel):
 
 def stage_kernel(cfg, stage):
     """Name of the one kernel a stage launches on this workload's path."""
-    T, mfma = cfg.tokens, (cfg.hidden >= 256 and cfg.ffn >= 256)
+    T = cfg.tokens
+    # 2-bit batches take the MFMA GEMMs from 64 tokens (the library's kMfmaMinTokensQ2)
+    mfma = cfg.hidden >= 256 and cfg.ffn >= 256 and (cfg.routed_fmt == "q8" or T >= 64)
     if T <= 32:
         return {"route": "decode_front_kernel", "select": "decode_select_kernel",
                 "gateup": "decode_gateup1_kernel" if T == 1 else "gateup_vec_kernel",
@@ -171,7 +173,7 @@ def stage_model(cfg, qr, u_avg):
         # 2-bit experts: the gate/up GEMM reads x's subblock sums and stores
         # h's, which the down GEMM reads
         xs16 = T * (H // 16) * 4 if cfg.routed_fmt == "q2" else 0
-        hs16 = Pr * (F // 16) * 4 if cfg.routed_fmt == "q2" else 0
+        hs16 = Pr * (F // 16) * 4 if cfg.routed_fmt == "q2" and T >= 64 else 0
         st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + xs16 + hq(P) + hs16
         st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + hs16 + P * H * 4
         st["combine"] = P * H * 4 + x32

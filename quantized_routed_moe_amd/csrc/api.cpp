@@ -24,6 +24,12 @@ int hip_status(hipError_t e) {
 
 constexpr size_t kAlign = 256;
 constexpr int kMfmaTile = 64;  // pairs per MFMA work tile
+// Smallest batch whose 2-bit experts take the MFMA GEMMs (Q8: every batch
+// past the decode sizes).  A tile's compute time is fixed however few pairs
+// it holds, and the 2-bit body's is the larger; measured at H 4096, 256
+// experts top-6, F 2048: 33 tokens 412 us on the VALU kernels vs 543 us on
+// the GEMMs, 48 tokens 491 vs 590, 64 tokens 584 vs 593, 128 tokens 949 vs 657.
+constexpr int kMfmaMinTokensQ2 = 64;
 
 inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -91,7 +97,7 @@ Layout make_layout(const moe_shape *s, int64_t T) {
     L.hq = take(P * F);
     L.hd = take(P * (F / 32) * 4);
     // the 2-bit down GEMM of batches past the decode sizes reads h's subblock sums
-    L.hs16 = take(s->routed_fmt == MOE_FMT_Q2_256 && T > kDecodeMaxT ? P * (F / 16) * 4 : 0);
+    L.hs16 = take(s->routed_fmt == MOE_FMT_Q2_256 && T >= kMfmaMinTokensQ2 ? P * (F / 16) * 4 : 0);
     L.y = take(P * H * 4);
     L.total = o;
     return L;
@@ -221,8 +227,9 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
         }
     } else {
         // Q8 and 2-bit experts go through the grouped int8 MFMA GEMMs (64-pair
-        // tiles); the smallest shapes stay on the VALU kernels.
-        const bool mfma = H >= 256 && shape->ffn >= 256;
+        // tiles); the smallest shapes, and 2-bit batches below
+        // kMfmaMinTokensQ2, stay on the VALU kernels.
+        const bool mfma = H >= 256 && shape->ffn >= 256 && (!q2 || T >= kMfmaMinTokensQ2);
         const int64_t tiles = mfma ? max_groups(shape, T, kMfmaTile) : mg;
         a.group_tok = mfma ? kMfmaTile : kVecTok;
         run(MOE_STAGE_QUANT, [&] { return launch_quant(a, s); });

@@ -144,7 +144,10 @@ SMALL = [
     ms.LayerConfig("q8_learned_512_T100", 512, 32, 4, 256, 100, seed=14),
     ms.LayerConfig("q2_learned_512", 512, 32, 4, 512, 9, routed_fmt="q2", seed=15),
     ms.LayerConfig("q2_learned_1024_T40", 1024, 24, 3, 512, 40, routed_fmt="q2", seed=16),
+    # 2-bit batches: the VALU kernels up to 63 tokens, the MFMA GEMMs from 64
     ms.LayerConfig("q2_learned_512_T33", 512, 32, 4, 512, 33, routed_fmt="q2", seed=68),
+    ms.LayerConfig("q2_learned_512_T63", 512, 32, 4, 512, 63, routed_fmt="q2", seed=69),
+    ms.LayerConfig("q2_mfma_512_T64", 512, 32, 4, 512, 64, routed_fmt="q2", seed=70),
     ms.LayerConfig("q8_hash_256", 256, 16, 2, 128, 3, route="hash", vocab=1000, seed=17),
     ms.LayerConfig("q8_hash_256_T50", 256, 16, 2, 128, 50, route="hash", vocab=1000, seed=18),
     ms.LayerConfig("q8_noshared_k1", 256, 8, 1, 256, 5, shared=False, seed=19),
@@ -162,7 +165,7 @@ SMALL = [
     # 2-bit routed experts on the MFMA GEMMs (the shared expert Q8 in the same launches)
     ms.LayerConfig("q2_mfma_512_T300", 512, 16, 4, 512, 300, routed_fmt="q2", seed=64),
     ms.LayerConfig("q2_mfma_hash_T77", 1024, 64, 6, 512, 77, routed_fmt="q2", route="hash", vocab=5000, seed=65),
-    ms.LayerConfig("q2_mfma_noshared_T45", 512, 8, 3, 1024, 45, routed_fmt="q2", shared=False, seed=66),
+    ms.LayerConfig("q2_mfma_noshared_T66", 512, 8, 3, 1024, 66, routed_fmt="q2", shared=False, seed=66),
     # routing variants: score-weighted hash, hash rows wider than top-k, 384 experts top-8
     ms.LayerConfig("q8_hashscored_T1", 512, 32, 6, 256, 1, route="hash_scored", vocab=300, seed=50),
     ms.LayerConfig("q8_hashscored_reduced_T9", 512, 32, 4, 256, 9, route="hash_scored", vocab=300, table_k=6,
@@ -280,12 +283,14 @@ def test_empty_batch_is_a_no_op():
                                  ms.LayerConfig("batch_learned_T3", 1024, 64, 6, 512, 3, seed=36),
                                  ms.LayerConfig("batch_hash", 512, 32, 4, 256, 12, route="hash", vocab=300,
                                                 seed=32),
-                                 ms.LayerConfig("batch_q2_T32", 512, 32, 4, 512, 32, routed_fmt="q2", seed=35)],
+                                 ms.LayerConfig("batch_q2_T32", 512, 32, 4, 512, 32, routed_fmt="q2", seed=35),
+                                 ms.LayerConfig("batch_q2_T40", 512, 32, 4, 512, 40, routed_fmt="q2", seed=35)],
                          ids=lambda c: c.name)
 def test_batched_equals_single_token_calls_bitwise(cfg):
-    """Batches the VALU expert kernels serve (up to 32 tokens) give every token
-    the bits of a one-token call.  (Longer batches run the MFMA GEMMs, which
-    accumulate in another order; they are held to the oracle tolerance.)"""
+    """Batches the VALU expert kernels serve (up to 32 tokens; 2-bit experts up
+    to 63, past 32 with the batched routing kernels) give every token the bits
+    of a one-token call.  (Batches on the MFMA GEMMs accumulate in another
+    order; they are held to the oracle tolerance.)"""
     inp, layer = case(cfg)
     x = torch.from_numpy(inp["x"]).cuda()
     tok = torch.from_numpy(inp["token_ids"]).cuda() if cfg.route != "learned" else None
