@@ -4,8 +4,8 @@
 // block sums with v_dot4c_i32_i8, then the two block scales in fp32 (the
 // quantized matvec path of "DwarfStar (ds4) — ROCm / gfx1151 fork",
 // Performance optimizations: moe_gate_up_mid_* / moe_down_* and the q8_0
-// "preq" matvecs).  Used for batches of 2..32 tokens and for 2-bit experts
-// at any batch size.
+// "preq" matvecs).  Used for batches of 2..32 tokens (2-bit experts: up to
+// 63), and for shapes below the MFMA GEMMs' minimum.
 //
 // Work list: groups {expert (E = shared), first index, count <= 8}; grid =
 // (row chunks of 32 rows) x (groups).  Workgroups beyond the device-side
