@@ -114,10 +114,19 @@ def stage_kernel(cfg, stage):
     # 2-bit batches take the MFMA GEMMs from 64 tokens (the library's kMfmaMinTokensQ2)
     mfma = cfg.hidden >= 256 and cfg.ffn >= 256 and (cfg.routed_fmt == "q8" or T >= 64)
     if T <= 32:
+        # selection of 2..32 tokens: one workgroup up to 8 tokens (learned) or 20
+        # (hash routes), else one wave per token and the sort kernel
+        dsel = T <= (8 if cfg.route == "learned" else 20)
+        if T > 1 and not dsel and stage in ("select", "sort"):
+            return {"select": "select_kernel", "sort": "sort_kernel"}[stage]
         return {"route": "decode_front_kernel", "select": "decode_select_kernel",
                 "gateup": "decode_gateup1_kernel" if T == 1 else "gateup_vec_kernel",
                 "down": "decode_down1_kernel" if T == 1 else "down_vec_kernel",
                 "combine": "combine_kernel"}.get(stage)
+    if T <= 224:  # the library's kFrontMaxTokens: quantization and logits in the decode front kernel
+        front = {"route": "decode_front_kernel", "quant": None, "logits": None}
+        if stage in front:
+            return front[stage]
     return {"quant": "quant_kernel", "logits": "logits_tiled_kernel", "select": "select_kernel",
             "sort": "sort_kernel" if T * cfg.top_k <= 4096 else "sort_scatter_kernel", "gateup": "gateup_mfma_kernel" if mfma else "gateup_vec_kernel",
             "down": "down_mfma_kernel" if mfma else "down_vec_kernel", "combine": "combine_kernel"}.get(stage)
@@ -158,6 +167,8 @@ def stage_model(cfg, qr, u_avg):
             st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P) + sel
         else:
             st["select"] = sel
+            if T > (8 if cfg.route == "learned" else 20):
+                st["sort"] = T * k * 4 * 3
             st["gateup"] = u_avg * 2 * mr_gu + sh * 2 * mq8_gu + xq + hq(P)
         if T == 1:
             st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + x32
@@ -165,9 +176,12 @@ def stage_model(cfg, qr, u_avg):
             st["down"] = u_avg * mr_dn + sh * mq8_dn + hq(P) + P * H * 4
             st["combine"] = P * H * 4 + x32
     else:
-        st["quant"] = x32 + xq
-        if has_router:
-            st["logits"] = router + x32 + rout
+        if T <= 224:  # decode front kernel: quantization and logits in one launch
+            st["route"] = router + x32 + xq + rout
+        else:
+            st["quant"] = x32 + xq
+            if has_router:
+                st["logits"] = router + x32 + rout
         st["select"] = (2 * T * E * 4 if has_router else T * 4) + T * k * 8
         st["sort"] = T * k * 4 * 3
         # 2-bit experts: the gate/up GEMM reads x's subblock sums and stores

@@ -30,6 +30,20 @@ constexpr int kMfmaTile = 64;  // pairs per MFMA work tile
 // experts top-6, F 2048: 33 tokens 412 us on the VALU kernels vs 543 us on
 // the GEMMs, 48 tokens 491 vs 590, 64 tokens 584 vs 593, 128 tokens 949 vs 657.
 constexpr int kMfmaMinTokensQ2 = 64;
+// Largest batch past the decode sizes whose quantization and router logits
+// run in the decode front kernel (one logit per workgroup).  The 32x32-tile
+// logits kernel's grid fills the chip only for long batches; measured at H
+// 4096, 256 experts (quantization + logits): 33 tokens 20 us vs 123 us tiled,
+// 128 tokens 68 vs 124, 192 tokens 98 vs 124, 256 tokens 128 vs 124.  Both
+// compute the same tree, so the results are the same bits.
+constexpr int kFrontMaxTokens = 224;
+// Largest decode batch whose selection, sort and work list run in the
+// one-workgroup decode select kernel; past it, one wave per token selects
+// (select_kernel) and the sort kernel builds the work list.  Measured
+// (select + sort, 4096 hidden, 256 experts top-6): learned 8 tokens 8.4 us vs
+// 8.3, 12 tokens 11.0 vs 8.3, 32 tokens 25.8 vs 8.6; hash 16 tokens 7.4 vs
+// 8.5, 24 tokens 9.6 vs 8.4, 32 tokens 11.4 vs 8.4.  Same results either way.
+constexpr int kDecodeSelectMaxLearned = 8, kDecodeSelectMaxHash = 20;
 
 inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -220,7 +234,12 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
             run(MOE_STAGE_GATEUP, [&] { return launch_decode_gateup1(a, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_decode_down1(a, dump, s); });
         } else {
-            run(MOE_STAGE_SELECT, [&] { return launch_decode_select(a, s); });
+            if (T <= (shape->route == MOE_ROUTE_LEARNED ? kDecodeSelectMaxLearned : kDecodeSelectMaxHash)) {
+                run(MOE_STAGE_SELECT, [&] { return launch_decode_select(a, s); });
+            } else {
+                run(MOE_STAGE_SELECT, [&] { return launch_select(a, s); });
+                run(MOE_STAGE_SORT, [&] { return launch_sort(a, s); });
+            }
             run(MOE_STAGE_GATEUP, [&] { return launch_gateup_vec(a, (int)mg, dump, s); });
             run(MOE_STAGE_DOWN, [&] { return launch_down_vec(a, (int)mg, dump, s); });
             run(MOE_STAGE_COMBINE, [&] { return launch_combine(a, s); });
@@ -232,8 +251,12 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
         const bool mfma = H >= 256 && shape->ffn >= 256 && (!q2 || T >= kMfmaMinTokensQ2);
         const int64_t tiles = mfma ? max_groups(shape, T, kMfmaTile) : mg;
         a.group_tok = mfma ? kMfmaTile : kVecTok;
-        run(MOE_STAGE_QUANT, [&] { return launch_quant(a, s); });
-        if (router) run(MOE_STAGE_LOGITS, [&] { return launch_logits(a, s); });
+        if (T <= kFrontMaxTokens) {
+            run(MOE_STAGE_ROUTE, [&] { return launch_decode_front(a, s); });
+        } else {
+            run(MOE_STAGE_QUANT, [&] { return launch_quant(a, s); });
+            if (router) run(MOE_STAGE_LOGITS, [&] { return launch_logits(a, s); });
+        }
         run(MOE_STAGE_SELECT, [&] { return launch_select(a, s); });
         run(MOE_STAGE_SORT, [&] { return launch_sort(a, s); });
         if (mfma) {

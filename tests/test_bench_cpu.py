@@ -42,9 +42,19 @@ def test_stage_kernels_follow_the_dispatch(bench):
     assert bench.stage_kernel(c["decode_q8"], "gateup") == "decode_gateup1_kernel"
     assert bench.stage_kernel(c["decode_q8"], "down") == "decode_down1_kernel"
     assert bench.stage_kernel(c["hash_decode"], "gateup") == "gateup_vec_kernel"
+    # 32 hash-routed tokens: one wave per token selects, the sort kernel builds the work list
+    assert bench.stage_kernel(c["hash_decode"], "select") == "select_kernel"
+    assert bench.stage_kernel(c["hash_decode"], "sort") == "sort_kernel"
+    small = ms.LayerConfig("small", 4096, 256, 6, 2048, 8)
+    assert bench.stage_kernel(small, "select") == "decode_select_kernel" and bench.stage_kernel(small, "sort") is None
     assert bench.stage_kernel(c["prefill"], "gateup") == "gateup_mfma_kernel"
     assert bench.stage_kernel(c["prefill"], "down") == "down_mfma_kernel"
     assert bench.stage_kernel(c["prefill_q2"], "gateup") == "gateup_mfma_kernel"
+    # past the decode sizes, up to 224 tokens: quantization and logits in the front kernel
+    mid = ms.LayerConfig("mid", 4096, 256, 6, 2048, 100)
+    assert bench.stage_kernel(mid, "route") == "decode_front_kernel"
+    assert bench.stage_kernel(mid, "logits") is None and bench.stage_kernel(mid, "select") == "select_kernel"
+    assert bench.stage_kernel(c["prefill"], "logits") == "logits_tiled_kernel"
     # 2048 tokens x top-6 = 12,288 pairs: the chunked sort
     assert bench.stage_kernel(c["prefill"], "sort") == "sort_scatter_kernel"
     every = set(bench.KERNEL_SOURCES)

@@ -171,6 +171,10 @@ SMALL = [
     ms.LayerConfig("q8_hashscored_reduced_T9", 512, 32, 4, 256, 9, route="hash_scored", vocab=300, table_k=6,
                    seed=51),
     ms.LayerConfig("q8_hashscored_T70", 512, 64, 6, 256, 70, route="hash_scored", vocab=5000, seed=52),
+    # the batched routing's two front ends: the decode front kernel up to 224 tokens, the tiled logits above
+    ms.LayerConfig("q8_front_T224", 512, 64, 6, 256, 224, seed=71),
+    ms.LayerConfig("q8_tiled_T225", 512, 64, 6, 256, 225, seed=72),
+    ms.LayerConfig("q8_hashscored_T230", 512, 64, 6, 256, 230, route="hash_scored", vocab=5000, seed=73),
     ms.LayerConfig("q2_hash_reduced_T1", 512, 16, 4, 512, 1, routed_fmt="q2", route="hash", vocab=50, table_k=6,
                    seed=53),
     ms.LayerConfig("q8_hash_reduced_T40", 512, 32, 2, 256, 40, route="hash", vocab=400, table_k=6, seed=54),
@@ -238,7 +242,7 @@ def test_chunked_sort_ragged_and_skewed(skew):
     check(cfg, inp, g, rows=np.r_[0:6, 500:506, 1094:1100], stride=8, name=cfg.name)
 
 
-@pytest.mark.parametrize("T", [1, 7, 40])
+@pytest.mark.parametrize("T", [1, 7, 12, 40])
 def test_tied_keys_take_the_smaller_expert_ids(T):
     """Experts share router rows and biases in groups of four, so every
     token's top-6 boundary falls inside a group of equal keys: the two
