@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_TOKENS 16384 /* tokens per call; larger batches are refused, not split */
 
 typedef enum moe_status {
@@ -58,7 +58,8 @@ typedef enum moe_status {
     MOE_ERR_WORKSPACE = -4,       /* workspace smaller than moe_workspace_bytes() or misaligned */
     MOE_ERR_HIP = -5,             /* a HIP runtime call or kernel launch failed */
     MOE_ERR_BAD_TABLE = -6,       /* hash table entry out of range or repeated within a row */
-    MOE_ERR_BAD_TOKEN = -7        /* a token id outside [0, vocab) was seen (moe_workspace_flags) */
+    MOE_ERR_BAD_TOKEN = -7,       /* a token id outside [0, vocab) was seen (moe_workspace_flags) */
+    MOE_ERR_NOT_PREPARED = -8     /* a context forward before a successful moe_prepare */
 } moe_status;
 
 /* Weight storage formats (canonical, little-endian, row-major [rows][cols]):
@@ -127,7 +128,7 @@ typedef struct moe_debug {
     int8_t *hq;        /* [P][F] quantized h, P = T*k + T*has_shared */
     float *hd;         /* [P][F/32] h block scales */
     /* Exact integer block sums of sampled weight rows (rows r with
-     * r % sum_row_stride == 0, stride a power of two <= 32): Q8 per 32-block,
+     * r % sum_row_stride == 0, stride a power of two <= min(H, F)): Q8 per 32-block,
      * Q2 per 16-weight subblock.  gate_sums/up_sums [P][F/stride][W_h],
      * down_sums [P][H/stride][W_f] with W_h = H/16, W_f = F/16 when the routed
      * experts are Q2_256 and H/32, F/32 otherwise; a Q8_32 pair (the shared
@@ -187,10 +188,65 @@ int moe_layer_forward_debug(const moe_shape *shape, const moe_weights *weights, 
  * Required once after allocating a workspace, before its first forward call. */
 int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
-/* Read the sticky device-side flags of a workspace: bit 0 = a token id was
- * outside [0, vocab), bit 1 = a hash-table entry was outside [0, E).  They
- * stay set until moe_workspace_init.  Synchronises `stream`. */
+/* Read the sticky device-side flags of a workspace (MOE_FLAG_* bits): a
+ * token id outside [0, vocab) (clamped to row 0), a hash-table entry outside
+ * [0, E) (clamped to expert 0), or a kept hash-table row that names one
+ * expert twice.  The last two describe a table that moe_check_hash_table
+ * rejects; the layer still runs without faulting, but a repeated expert is
+ * weighted once where the row names it twice, so that call's output is not
+ * the layer's.  The flags stay set until moe_workspace_init.  Synchronises
+ * `stream`. */
+enum { MOE_FLAG_BAD_TOKEN = 1, MOE_FLAG_BAD_TABLE_ENTRY = 2, MOE_FLAG_REPEATED_EXPERT = 4 };
 int moe_workspace_flags(void *workspace, int32_t *flags, void *stream);
+
+/* ------------------------------------------------- library-owned layers
+ * A context owns everything one layer needs between forward calls: a
+ * workspace sized for max_tokens, packed copies of the expert banks, and
+ * copies of the router weights, bias and hash table.  The lifecycle is
+ * create -> prepare (once per set of weights) -> forward (any number of
+ * times) -> destroy, the load-time preparation and fenced forward of "ds4:
+ * dfm Edition" (About this fork: aligned artifacts built in-process at load;
+ * Benchmarking: typed refusals instead of silent fallbacks), behind a plain C
+ * handle as in "Working on the ds4 Backend" (Wire shape: engine open, session
+ * create).  The caller-workspace calls above stay available for callers that
+ * manage memory themselves.
+ *
+ * A context lives on the device current at moe_ctx_create (moe_prepare and
+ * moe_ctx_forward return MOE_ERR_INVALID_ARG when another device is current)
+ * and is used from one stream at a time.  It allocates device memory (hipMalloc) only in
+ * moe_ctx_create and the first moe_prepare, and frees it in moe_ctx_destroy. */
+typedef struct moe_ctx moe_ctx;
+
+/* Validate the shape (MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED), allocate a
+ * workspace for batches of up to max_tokens (1..MOE_MAX_TOKENS) and enqueue
+ * its initialisation on `stream`.  *ctx is set only on success. */
+int moe_ctx_create(const moe_shape *shape, int32_t max_tokens, moe_ctx **ctx, void *stream);
+
+/* Load one set of weights into the context.  `canonical` holds device
+ * pointers in the CANONICAL formats above (gate/up/down banks of E matrices,
+ * the shared expert's three Q8_32 matrices, router weights [E][H] fp32, bias
+ * [E] fp32 or NULL, hash table [vocab][table_k or top_k] int32), 16-byte
+ * aligned; they are only read during this call.  The banks are repacked into
+ * library-owned memory, router, bias and table are copied, and the table is
+ * validated (every kept entry in [0, E), no expert twice in a row): a bad
+ * table returns MOE_ERR_BAD_TABLE and leaves the context unprepared, so no
+ * forward call runs on it.  Synchronises `stream`.  A later moe_prepare
+ * replaces the weights in place. */
+int moe_prepare(moe_ctx *ctx, const moe_weights *canonical, void *stream);
+
+/* moe_layer_forward on the context's weights and workspace: out[T][H] from
+ * x[T][H], token_ids [T] for the hash routes.  MOE_ERR_NOT_PREPARED before a
+ * successful moe_prepare; MOE_ERR_TOO_MANY_TOKENS when tokens > max_tokens. */
+int moe_ctx_forward(moe_ctx *ctx, const float *x, const int32_t *token_ids, int32_t tokens, float *out,
+                    void *stream);
+
+/* The context workspace's sticky flags (moe_workspace_flags); reset = 1
+ * clears them after reading.  Synchronises `stream`. */
+int moe_ctx_flags(moe_ctx *ctx, int32_t *flags, int32_t reset, void *stream);
+
+/* Free the context and everything it owns (waits for its pending work).
+ * NULL is a no-op. */
+void moe_ctx_destroy(moe_ctx *ctx);
 
 /* Per-stage timing with HIP events.  While a profiler is attached to the
  * calling thread, every kernel a forward call launches records its own start

@@ -30,6 +30,8 @@ ROUTE_LEARNED, ROUTE_HASH, ROUTE_HASH_SCORED = 1, 2, 3
 FMT = {"q8": FMT_Q8, "q2": FMT_Q2}
 ROUTE = {"learned": ROUTE_LEARNED, "hash": ROUTE_HASH, "hash_scored": ROUTE_HASH_SCORED}
 STAGES = ["route", "quant", "logits", "select", "sort", "gateup", "down", "combine"]
+# sticky workspace flags (moe_workspace_flags)
+FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_REPEATED_EXPERT = 1, 2, 4
 ALIGN = 256
 
 
@@ -73,6 +75,11 @@ _SIGS = {
                           ctypes.c_int),
     "moe_layer_forward_debug": ([ctypes.POINTER(Shape), ctypes.POINTER(Weights), _P, _P, _I32, _P, _P, _SZ,
                                  ctypes.POINTER(Debug), _P], ctypes.c_int),
+    "moe_ctx_create": ([ctypes.POINTER(Shape), _I32, ctypes.POINTER(_P), _P], ctypes.c_int),
+    "moe_prepare": ([_P, ctypes.POINTER(Weights), _P], ctypes.c_int),
+    "moe_ctx_forward": ([_P, _P, _P, _I32, _P, _P], ctypes.c_int),
+    "moe_ctx_flags": ([_P, ctypes.POINTER(_I32), _I32, _P], ctypes.c_int),
+    "moe_ctx_destroy": ([_P], None),
     "moe_stage_name": ([_I32], ctypes.c_char_p),
     "moe_prof_create": ([ctypes.POINTER(_P), _I32], ctypes.c_int),
     "moe_prof_destroy": ([_P], None),
@@ -160,6 +167,44 @@ def layer_forward(shape: Shape, weights: Weights, x, token_ids, out, ws, stream=
     return out
 
 
+class Context:
+    """A library-owned layer (moe_ctx_*): the library allocates the workspace
+    and the packed weights, validates the hash table at prepare and refuses
+    forward calls until a prepare succeeded."""
+
+    def __init__(self, shape: Shape, max_tokens: int, stream=None):
+        self.shape = shape
+        self._h = _P()
+        _check(_lib.moe_ctx_create(ctypes.byref(shape), max_tokens, ctypes.byref(self._h), _stream(stream)),
+               "moe_ctx_create")
+
+    def prepare(self, canonical: Weights, stream=None):
+        """canonical: device pointers to the canonical weight bytes (see moe.h)."""
+        _check(_lib.moe_prepare(self._h, ctypes.byref(canonical), _stream(stream)), "moe_prepare")
+
+    def forward(self, x, token_ids, out, stream=None):
+        T = x.shape[0] if x.dim() == 2 else 0
+        _check(_lib.moe_ctx_forward(self._h, _ptr(x), _ptr(token_ids), T, _ptr(out), _stream(stream)),
+               "moe_ctx_forward")
+        return out
+
+    def flags(self, reset: bool = False, stream=None) -> int:
+        f = _I32(0)
+        _check(_lib.moe_ctx_flags(self._h, ctypes.byref(f), 1 if reset else 0, _stream(stream)), "moe_ctx_flags")
+        return f.value
+
+    def close(self):
+        if self._h:
+            _lib.moe_ctx_destroy(self._h)
+            self._h = _P()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class Profiler:
     """Per-stage HIP-event timing of the forward calls made while attached."""
 
@@ -193,7 +238,7 @@ class Profiler:
 
 from .layer import MoELayer  # noqa: E402
 
-__all__ = ["MoELayer", "MoEError", "Shape", "Weights", "Debug", "Profiler", "make_shape", "workspace_bytes",
+__all__ = ["MoELayer", "MoEError", "Context", "Shape", "Weights", "Debug", "Profiler", "make_shape", "workspace_bytes",
            "pack_weights", "layer_forward", "workspace_init", "workspace_flags", "check_hash_table", "matrix_bytes",
-           "abi_version", "FMT_Q8", "FMT_Q2", "ROUTE_LEARNED", "ROUTE_HASH", "ROUTE_HASH_SCORED", "EXPORTED",
+           "abi_version", "FMT_Q8", "FMT_Q2", "FLAG_BAD_TOKEN", "FLAG_BAD_TABLE_ENTRY", "FLAG_REPEATED_EXPERT", "ROUTE_LEARNED", "ROUTE_HASH", "ROUTE_HASH_SCORED", "EXPORTED",
            "LIB_PATH"]

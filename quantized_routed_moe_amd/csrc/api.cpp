@@ -131,38 +131,29 @@ struct moe_prof {
 };
 
 static thread_local moe_prof *t_prof = nullptr;
+static thread_local int t_stage = -1;  // stage of the forward call running on this thread, or -1
 
 namespace qrmoe {
-LaunchEvents &launch_events() {
-    static thread_local LaunchEvents ev;
-    return ev;
+bool next_launch_events(hipEvent_t *start, hipEvent_t *stop) {
+    moe_prof *p = t_prof;
+    if (!p || t_stage < 0 || p->next + 2 > p->pool.size()) return false;
+    *start = p->pool[p->next++];
+    *stop = p->pool[p->next++];
+    p->used.push_back(EventPair{*start, *stop, t_stage});
+    return true;
 }
 }  // namespace qrmoe
 
 namespace {
 
-// Launch helper: with a profiler attached, arms an event pair that the
-// stage's kernel launch records its start and end into.
+// Runs one stage's launches with the stage recorded for the profiler: each
+// kernel the stage launches is timed on its own (the chunked sort, for one,
+// launches three).
 template <class F>
-hipError_t timed(int stage, hipStream_t s, F &&launch) {
-    moe_prof *p = t_prof;
-    EventPair ev{nullptr, nullptr, stage};
-    LaunchEvents &armed = launch_events();
-    if (p && p->next + 2 <= p->pool.size()) {
-        ev.a = p->pool[p->next++];
-        ev.b = p->pool[p->next++];
-        armed.start = ev.a;
-        armed.stop = ev.b;
-    }
-    hipError_t err = launch();
-    if (ev.a) {
-        if (armed.start == nullptr) {
-            p->used.push_back(ev);  // the stage's kernel took the events
-        } else {
-            armed.start = armed.stop = nullptr;  // no kernel launched: return the pair
-            p->next -= 2;
-        }
-    }
+hipError_t timed(int stage, F &&launch) {
+    t_stage = stage;
+    const hipError_t err = launch();
+    t_stage = -1;
     return err;
 }
 
@@ -223,7 +214,7 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
 
     hipError_t err = hipSuccess;
     auto run = [&](int stage, auto &&fn) {
-        if (err == hipSuccess) err = timed(stage, s, fn);
+        if (err == hipSuccess) err = timed(stage, fn);
     };
     const int64_t mg = max_groups(shape, T, kVecTok);
     a.group_tok = kVecTok;
@@ -303,6 +294,7 @@ const char *moe_status_string(int status) {
         case MOE_ERR_HIP: return "HIP runtime error";
         case MOE_ERR_BAD_TABLE: return "invalid hash table";
         case MOE_ERR_BAD_TOKEN: return "token id out of range";
+        case MOE_ERR_NOT_PREPARED: return "context has no prepared weights";
         default: return "unknown status";
     }
 }
@@ -380,6 +372,159 @@ int moe_layer_forward_debug(const moe_shape *shape, const moe_weights *weights, 
     if (!dbg) return MOE_ERR_INVALID_ARG;
     return forward_impl(shape, weights, x, token_ids, tokens, out, workspace, workspace_bytes, dbg, stream);
 }
+
+}  // extern "C"
+
+// ------------------------------------------------- library-owned layers
+struct moe_ctx {
+    moe_shape shape{};
+    int32_t max_tokens = 0;
+    int device = 0;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    // library-owned weights: packed banks, router, bias and table copies
+    void *gate = nullptr, *up = nullptr, *down = nullptr;
+    void *sh_gate = nullptr, *sh_up = nullptr, *sh_down = nullptr;
+    void *router_w = nullptr, *router_b = nullptr, *table = nullptr;
+    bool prepared = false;
+};
+
+namespace {
+
+void ctx_free_weights(moe_ctx *c) {
+    for (void **p : {&c->gate, &c->up, &c->down, &c->sh_gate, &c->sh_up, &c->sh_down, &c->router_w, &c->router_b,
+                     &c->table}) {
+        if (*p) (void)hipFree(*p);
+        *p = nullptr;
+    }
+}
+
+// Device buffer of `bytes` owned by the context, allocated on first use and
+// reused by later prepares (a context's shape fixes every size).
+hipError_t ctx_buffer(void **p, size_t bytes) {
+    if (*p) return hipSuccess;
+    return hipMalloc(p, bytes == 0 ? 1 : bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ctx_create(const moe_shape *shape, int32_t max_tokens, moe_ctx **ctx, void *stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const int st = validate_shape(shape);
+    if (st != MOE_OK) return st;
+    if (max_tokens < 1) return MOE_ERR_INVALID_ARG;
+    if (max_tokens > MOE_MAX_TOKENS) return MOE_ERR_TOO_MANY_TOKENS;
+    moe_ctx *c = new moe_ctx();
+    c->shape = *shape;
+    c->max_tokens = max_tokens;
+    c->ws_bytes = make_layout(shape, max_tokens).total;
+    hipError_t err = hipGetDevice(&c->device);
+    if (err == hipSuccess) err = hipMalloc(&c->ws, c->ws_bytes);
+    if (err == hipSuccess) err = launch_ws_init((int32_t *)c->ws, kCtlWords, (hipStream_t)stream);
+    if (err != hipSuccess) {
+        if (c->ws) (void)hipFree(c->ws);
+        delete c;
+        return hip_status(err);
+    }
+    *ctx = c;
+    return MOE_OK;
+}
+
+int moe_prepare(moe_ctx *c, const moe_weights *w, void *stream) {
+    if (!c || !w) return MOE_ERR_INVALID_ARG;
+    const moe_shape &sh = c->shape;
+    const bool router = sh.route != MOE_ROUTE_HASH, hashed = sh.route != MOE_ROUTE_LEARNED;
+    if (router && !w->router_w) return MOE_ERR_INVALID_ARG;
+    if (sh.route != MOE_ROUTE_LEARNED && w->router_b) return MOE_ERR_INVALID_ARG;
+    if (hashed && !w->hash_table) return MOE_ERR_INVALID_ARG;
+    if (!w->gate || !w->up || !w->down) return MOE_ERR_INVALID_ARG;
+    if (sh.has_shared && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_INVALID_ARG;
+    if (!sh.has_shared && (w->sh_gate || w->sh_up || w->sh_down)) return MOE_ERR_INVALID_ARG;
+    const void *al16[] = {w->router_w, w->router_b, w->hash_table, w->gate,   w->up,
+                          w->down,     w->sh_gate,  w->sh_up,      w->sh_down};
+    for (const void *p : al16)
+        if (p && !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return MOE_ERR_INVALID_ARG;
+    c->prepared = false;
+    const int64_t H = sh.hidden, E = sh.n_experts, F = sh.ffn;
+    const int32_t row_k = hashed && sh.table_k ? sh.table_k : sh.top_k;
+    const int64_t gu = moe_matrix_bytes(sh.routed_fmt, F, H), dn = moe_matrix_bytes(sh.routed_fmt, H, F);
+    const int64_t qgu = moe_matrix_bytes(MOE_FMT_Q8_32, F, H), qdn = moe_matrix_bytes(MOE_FMT_Q8_32, H, F);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err = hipSuccess;
+    auto step = [&](auto &&fn) {
+        if (err == hipSuccess) err = fn();
+    };
+    // the packed banks, from the canonical ones
+    auto pack = [&](void **dst, const void *src, int fmt, int64_t n, int64_t rows, int64_t cols, int64_t mb) {
+        step([&] { return ctx_buffer(dst, (size_t)(n * mb)); });
+        step([&] { return launch_pack(fmt, (const uint8_t *)src, (uint8_t *)*dst, n, rows, cols, s); });
+    };
+    pack(&c->gate, w->gate, sh.routed_fmt, E, F, H, gu);
+    pack(&c->up, w->up, sh.routed_fmt, E, F, H, gu);
+    pack(&c->down, w->down, sh.routed_fmt, E, H, F, dn);
+    if (sh.has_shared) {
+        pack(&c->sh_gate, w->sh_gate, MOE_FMT_Q8_32, 1, F, H, qgu);
+        pack(&c->sh_up, w->sh_up, MOE_FMT_Q8_32, 1, F, H, qgu);
+        pack(&c->sh_down, w->sh_down, MOE_FMT_Q8_32, 1, H, F, qdn);
+    }
+    auto copy = [&](void **dst, const void *src, size_t bytes) {
+        step([&] { return ctx_buffer(dst, bytes); });
+        step([&] { return hipMemcpyAsync(*dst, src, bytes, hipMemcpyDeviceToDevice, s); });
+    };
+    if (router) copy(&c->router_w, w->router_w, (size_t)(E * H * 4));
+    if (w->router_b) {
+        copy(&c->router_b, w->router_b, (size_t)E * 4);
+    } else if (c->router_b) {
+        (void)hipFree(c->router_b);  // no bias this time
+        c->router_b = nullptr;
+    }
+    if (hashed) copy(&c->table, w->hash_table, (size_t)sh.vocab * row_k * 4);
+    if (err != hipSuccess) return hip_status(err);
+    if (hashed) {
+        int32_t bad = -1;
+        const int st = moe_check_hash_table((const int32_t *)c->table, sh.vocab, row_k, (int32_t)E, c->ws,
+                                            c->ws_bytes, &bad, stream);
+        if (st != MOE_OK) return st;
+    }
+    step([&] { return hipStreamSynchronize(s); });
+    if (err != hipSuccess) return hip_status(err);
+    c->prepared = true;
+    return MOE_OK;
+}
+
+int moe_ctx_forward(moe_ctx *c, const float *x, const int32_t *token_ids, int32_t tokens, float *out,
+                    void *stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (!c->prepared) return MOE_ERR_NOT_PREPARED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return MOE_ERR_INVALID_ARG;
+    if (tokens > c->max_tokens) return MOE_ERR_TOO_MANY_TOKENS;
+    const moe_weights w{(const float *)c->router_w, (const float *)c->router_b, (const int32_t *)c->table,
+                        c->gate, c->up, c->down, c->sh_gate, c->sh_up, c->sh_down};
+    return forward_impl(&c->shape, &w, x, token_ids, tokens, out, c->ws, c->ws_bytes, nullptr, stream);
+}
+
+int moe_ctx_flags(moe_ctx *c, int32_t *flags, int32_t reset, void *stream) {
+    if (!c || !flags) return MOE_ERR_INVALID_ARG;
+    const int st = moe_workspace_flags(c->ws, flags, stream);
+    if (st != MOE_OK || !reset) return st;
+    return hip_status(launch_ws_init((int32_t *)c->ws, kCtlWords, (hipStream_t)stream));
+}
+
+void moe_ctx_destroy(moe_ctx *c) {
+    if (!c) return;
+    ctx_free_weights(c);
+    if (c->ws) (void)hipFree(c->ws);
+    delete c;
+}
+
+}  // extern "C"
+
+extern "C" {
 
 const char *moe_stage_name(int32_t stage) {
     static const char *names[MOE_N_STAGES] = {"route", "quant", "logits", "select", "sort", "gateup", "down", "combine"};

@@ -322,24 +322,19 @@ __device__ inline void block_excl_scan(const int *in, int *out, int n, int *tmp_
 }
 
 // ------------------------------------------------------------- launchers
-// Event pair armed by the stage profiler for the next layer kernel launch on
-// this thread.  A launch that finds it armed goes through
-// hipExtLaunchKernelGGL, whose events take the kernel's own start and end
-// times (no dispatch latency), and disarms it.
-struct LaunchEvents {
-    hipEvent_t start = nullptr, stop = nullptr;
-};
-LaunchEvents &launch_events();
+// While a stage profiler is attached to the calling thread and a forward call
+// runs one of its stages, every kernel launch takes its own pair of events
+// from the profiler (api.cpp) and goes through hipExtLaunchKernelGGL, whose
+// events take the kernel's own start and end times (no dispatch latency).
+bool next_launch_events(hipEvent_t *start, hipEvent_t *stop);
 
 template <class... KArgs, class... Args>
 void klaunch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
-    LaunchEvents &ev = launch_events();
-    if (ev.start) {
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
-        ev.start = ev.stop = nullptr;
-    } else {
+    hipEvent_t start, stop;
+    if (next_launch_events(&start, &stop))
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, args...);
+    else
         kernel<<<grid, block, 0, s>>>(args...);
-    }
 }
 
 hipError_t launch_pack(int fmt, const uint8_t *canon, uint8_t *packed, int64_t n_mats, int64_t rows, int64_t cols,

@@ -198,6 +198,13 @@ __device__ __forceinline__ void select_hash_regs(const int32_t *__restrict__ tok
         id_out = e;
         w_out = 1.0f / (float)k;
     }
+    // A kept row that names one expert twice (after clamping) is flagged: the
+    // layer then weights that expert once, where the row asks for it twice.
+    bool dup = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k) dup |= lane < k && j < lane && __builtin_amdgcn_readlane(id_out, j) == id_out;
+    if (__ballot(dup) != 0 && lane == 0) atomicOr(flags, 4);
     if (srow) {
         const float sc = lane < k ? srow[id_out] : 0.0f;
         float S = 0.0f;
@@ -233,9 +240,16 @@ __device__ __forceinline__ void select_hash_group8(const int32_t *__restrict__ t
     }
     id_out = e;
     w_out = mine ? 1.0f / (float)k : 0.0f;
+    const int base = lane & ~7;
+    bool dup = false;  // an expert repeated within the kept row, flagged as in select_hash_regs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int ei = __shfl(e, base + i);
+        dup |= mine && i < j && ei == e;
+    }
+    if (dup) atomicOr(flags, 4);
     if (scores) {
         const float sc = mine ? scores[(int64_t)t * E + e] : 0.0f;
-        const int base = lane & ~7;
         float S = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i)

@@ -105,6 +105,10 @@ class MoELayer:
     def flags(self) -> int:
         return workspace_flags(self.ws)
 
+    def reset_flags(self):
+        """Clear the workspace's sticky flags (and its other control words)."""
+        workspace_init(self.ws)
+
     # -------------------------------------------------------------- forward
     def forward(self, x: torch.Tensor, token_ids: torch.Tensor | None = None, out: torch.Tensor | None = None,
                 weights: Weights | None = None, stream=None) -> torch.Tensor:

@@ -29,8 +29,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert qr.abi_version() == 2
-    for st in range(-7, 1):
+    assert qr.abi_version() == 3
+    for st in range(-8, 1):
         assert L.moe_status_string(st) not in (None, b"unknown status")
     assert L.moe_status_string(-99) == b"unknown status"
 
@@ -141,3 +141,25 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__)))).stdout.split()
     assert len(out) == 1, out
+
+
+def test_context_calls_reject_bad_arguments_on_the_host():
+    """The context calls refuse NULL handles, bad shapes and token limits
+    before any HIP call (a valid shape would allocate, so none is used)."""
+    h = ctypes.c_void_p()
+    s = shape()
+    assert L.moe_ctx_create(ctypes.byref(s), 4, None, None) == INVALID
+    for bad in (dict(hidden=96), dict(top_k=9), dict(route=0), dict(routed_fmt="q2", hidden=256)):
+        st = L.moe_ctx_create(ctypes.byref(shape(**bad)), 4, ctypes.byref(h), None)
+        assert st in (INVALID, UNSUPPORTED), bad
+        assert not h.value
+    assert L.moe_ctx_create(ctypes.byref(s), 0, ctypes.byref(h), None) == INVALID
+    assert L.moe_ctx_create(ctypes.byref(s), 16385, ctypes.byref(h), None) == TOO_MANY
+    assert not h.value
+    w = good_weights()
+    assert L.moe_prepare(None, ctypes.byref(w), None) == INVALID
+    assert L.moe_ctx_forward(None, FAKE, None, 4, FAKE * 3, None) == INVALID
+    f = ctypes.c_int32(0)
+    assert L.moe_ctx_flags(None, ctypes.byref(f), 0, None) == INVALID
+    L.moe_ctx_destroy(None)
+    assert L.moe_status_string(-8) == b"context has no prepared weights"
