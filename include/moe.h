@@ -179,6 +179,23 @@ size_t moe_workspace_bytes(const moe_shape *shape, int32_t tokens);
 int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const float *x, const int32_t *token_ids,
                       int32_t tokens, float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_layer_forward without
+ * a workspace argument.  Its workspace is a fixed device array of
+ * MOE_STATIC_SCRATCH_BYTES inside the library, one copy per GPU, held until
+ * the process ends; the call allocates nothing.  A batch whose workspace
+ * (moe_workspace_bytes) exceeds it is refused with MOE_ERR_WORKSPACE before
+ * anything is enqueued (at hidden 4096, 256 experts top-6 and ffn 2048 the
+ * limit admits batches of up to 120 tokens).  The first call on a device
+ * looks up that device's copy and enqueues the clearing of its control words
+ * on `stream`.  Every call on one GPU shares its array: calls that overlap on
+ * one GPU (different streams, or threads without ordering) race and must not
+ * be issued.  Sticky flags are kept in the array but cannot be read through
+ * this entry point (out-of-range ids are still clamped). */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+int moe_layer_forward_static(const moe_shape *shape, const moe_weights *weights, const float *x,
+                             const int32_t *token_ids, int32_t tokens, float *out, void *stream);
+
 /* Same computation, plus copies of intermediates into `dbg`. */
 int moe_layer_forward_debug(const moe_shape *shape, const moe_weights *weights, const float *x,
                             const int32_t *token_ids, int32_t tokens, float *out, void *workspace,

@@ -32,6 +32,8 @@ ROUTE = {"learned": ROUTE_LEARNED, "hash": ROUTE_HASH, "hash_scored": ROUTE_HASH
 STAGES = ["route", "quant", "logits", "select", "sort", "gateup", "down", "combine"]
 # sticky workspace flags (moe_workspace_flags)
 FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_REPEATED_EXPERT = 1, 2, 4
+# bytes of the device array that serves moe_layer_forward_static as its workspace
+STATIC_SCRATCH_BYTES = 16 << 20
 ALIGN = 256
 
 
@@ -73,6 +75,8 @@ _SIGS = {
     "moe_workspace_flags": ([_P, ctypes.POINTER(_I32), _P], ctypes.c_int),
     "moe_layer_forward": ([ctypes.POINTER(Shape), ctypes.POINTER(Weights), _P, _P, _I32, _P, _P, _SZ, _P],
                           ctypes.c_int),
+    "moe_layer_forward_static": ([ctypes.POINTER(Shape), ctypes.POINTER(Weights), _P, _P, _I32, _P, _P],
+                                 ctypes.c_int),
     "moe_layer_forward_debug": ([ctypes.POINTER(Shape), ctypes.POINTER(Weights), _P, _P, _I32, _P, _P, _SZ,
                                  ctypes.POINTER(Debug), _P], ctypes.c_int),
     "moe_ctx_create": ([ctypes.POINTER(Shape), _I32, ctypes.POINTER(_P), _P], ctypes.c_int),
@@ -167,6 +171,14 @@ def layer_forward(shape: Shape, weights: Weights, x, token_ids, out, ws, stream=
     return out
 
 
+def layer_forward_static(shape: Shape, weights: Weights, x, token_ids, out, stream=None):
+    """moe_layer_forward_static: the layer on the library's per-GPU scratch array (allocates nothing)."""
+    T = x.shape[0] if x.dim() == 2 else 0
+    _check(_lib.moe_layer_forward_static(ctypes.byref(shape), ctypes.byref(weights), _ptr(x), _ptr(token_ids), T,
+                                         _ptr(out), _stream(stream)), "moe_layer_forward_static")
+    return out
+
+
 class Context:
     """A library-owned layer (moe_ctx_*): the library allocates the workspace
     and the packed weights, validates the hash table at prepare and refuses
@@ -239,6 +251,6 @@ class Profiler:
 from .layer import MoELayer  # noqa: E402
 
 __all__ = ["MoELayer", "MoEError", "Context", "Shape", "Weights", "Debug", "Profiler", "make_shape", "workspace_bytes",
-           "pack_weights", "layer_forward", "workspace_init", "workspace_flags", "check_hash_table", "matrix_bytes",
+           "pack_weights", "layer_forward", "layer_forward_static", "STATIC_SCRATCH_BYTES", "workspace_init", "workspace_flags", "check_hash_table", "matrix_bytes",
            "abi_version", "FMT_Q8", "FMT_Q2", "FLAG_BAD_TOKEN", "FLAG_BAD_TABLE_ENTRY", "FLAG_REPEATED_EXPERT", "ROUTE_LEARNED", "ROUTE_HASH", "ROUTE_HASH_SCORED", "EXPORTED",
            "LIB_PATH"]

@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -157,14 +158,17 @@ hipError_t timed(int stage, F &&launch) {
     return err;
 }
 
-int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x, const int32_t *token_ids,
-                 int32_t tokens, float *out, void *workspace, size_t ws_bytes, const moe_debug *dbg, void *stream) {
+// Host-side checks of a forward call's shape, weights, activations and debug
+// request (everything but the workspace).  MOE_OK for tokens == 0 without
+// looking at the pointers: the empty batch is a no-op.
+int check_forward_args(const moe_shape *shape, const moe_weights *wts, const float *x, const int32_t *token_ids,
+                       int32_t tokens, const float *out, const moe_debug *dbg) {
     int st = validate_shape(shape);
     if (st != MOE_OK) return st;
     if (tokens < 0) return MOE_ERR_INVALID_ARG;
     if (tokens > MOE_MAX_TOKENS) return MOE_ERR_TOO_MANY_TOKENS;
     if (tokens == 0) return MOE_OK;  // empty batch: nothing is read or written, buffers may be NULL
-    if (!wts || !x || !out || !workspace) return MOE_ERR_INVALID_ARG;
+    if (!wts || !x || !out) return MOE_ERR_INVALID_ARG;
     const bool router = shape->route != MOE_ROUTE_HASH;     // logits are computed
     const bool hashed = shape->route != MOE_ROUTE_LEARNED;  // experts come from the table
     if (router && !wts->router_w) return MOE_ERR_INVALID_ARG;
@@ -175,7 +179,6 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
     const void *al16[] = {x, out, wts->router_w, wts->gate, wts->up, wts->down, wts->sh_gate, wts->sh_up, wts->sh_down};
     for (const void *p : al16)
         if (p && !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
-    if (!aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
     const int64_t T = tokens, H = shape->hidden;
     {
         const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out, n = (uintptr_t)(T * H * 4);
@@ -184,6 +187,18 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
     if (dbg && (dbg->gate_sums || dbg->up_sums || dbg->down_sums) &&
         (!pow2(dbg->sum_row_stride) || dbg->sum_row_stride > shape->ffn || dbg->sum_row_stride > shape->hidden))
         return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x, const int32_t *token_ids,
+                 int32_t tokens, float *out, void *workspace, size_t ws_bytes, const moe_debug *dbg, void *stream) {
+    const int st = check_forward_args(shape, wts, x, token_ids, tokens, out, dbg);
+    if (st != MOE_OK || tokens == 0) return st;
+    if (!workspace) return MOE_ERR_INVALID_ARG;
+    if (!aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
+    const int64_t T = tokens, H = shape->hidden;
+    const bool router = shape->route != MOE_ROUTE_HASH;     // logits are computed
+    const bool hashed = shape->route != MOE_ROUTE_LEARNED;  // experts come from the table
     const Layout L = make_layout(shape, T);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
 
@@ -374,6 +389,54 @@ int moe_layer_forward_debug(const moe_shape *shape, const moe_weights *weights, 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------ allocation-free forward
+// The workspace of moe_layer_forward_static: a device array in the library's
+// code object, one copy per GPU.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels receive the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch`; on first use on a device, also
+// enqueue the clearing of its control words (a kernel, so the call may be
+// captured into a graph).
+hipError_t static_scratch(hipStream_t s, void **out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!ptr) return hipErrorInvalidSymbol;
+        err = launch_ws_init((int32_t *)ptr, kCtlWords, s);
+        if (err != hipSuccess) return err;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+extern "C" int moe_layer_forward_static(const moe_shape *shape, const moe_weights *weights, const float *x,
+                                        const int32_t *token_ids, int32_t tokens, float *out, void *stream) {
+    // every host-side check comes before the device lookup
+    const int st = check_forward_args(shape, weights, x, token_ids, tokens, out, nullptr);
+    if (st != MOE_OK || tokens == 0) return st;
+    if (make_layout(shape, tokens).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const hipError_t err = static_scratch((hipStream_t)stream, &ws);
+    if (err != hipSuccess) return hip_status(err);
+    return forward_impl(shape, weights, x, token_ids, tokens, out, ws, MOE_STATIC_SCRATCH_BYTES, nullptr, stream);
+}
 
 // ------------------------------------------------- library-owned layers
 struct moe_ctx {

@@ -163,3 +163,23 @@ def test_context_calls_reject_bad_arguments_on_the_host():
     assert L.moe_ctx_flags(None, ctypes.byref(f), 0, None) == INVALID
     L.moe_ctx_destroy(None)
     assert L.moe_status_string(-8) == b"context has no prepared weights"
+
+
+def test_static_forward_refuses_before_touching_the_device():
+    """moe_layer_forward_static validates every argument, and refuses a batch
+    whose workspace exceeds the static scratch, before it looks up the
+    device array (there is no device here: a lookup would fail as a HIP
+    error instead)."""
+    s = shape()
+    w = good_weights()
+    assert qr.workspace_bytes(s, 120) <= qr.STATIC_SCRATCH_BYTES < qr.workspace_bytes(s, 121)
+    assert L.moe_layer_forward_static(ctypes.byref(s), ctypes.byref(w), FAKE, None, 121, FAKE * 3, None) == WORKSPACE
+    assert L.moe_layer_forward_static(ctypes.byref(s), ctypes.byref(w), FAKE, None, 16385, FAKE * 3,
+                                      None) == TOO_MANY
+    assert L.moe_layer_forward_static(ctypes.byref(s), ctypes.byref(w), None, None, 4, FAKE * 3, None) == INVALID
+    assert L.moe_layer_forward_static(ctypes.byref(s), None, FAKE, None, 4, FAKE * 3, None) == INVALID
+    assert L.moe_layer_forward_static(ctypes.byref(shape(hidden=96)), ctypes.byref(w), FAKE, None, 4, FAKE * 3,
+                                      None) == UNSUPPORTED
+    assert L.moe_layer_forward_static(ctypes.byref(s), ctypes.byref(w), FAKE, None, 0, FAKE * 3, None) == OK
+    # out overlapping x
+    assert L.moe_layer_forward_static(ctypes.byref(s), ctypes.byref(w), FAKE, None, 4, FAKE + 16, None) == INVALID
