@@ -9,13 +9,17 @@ workload is the Q8 decode layer (1 token, hidden 4096, 256 experts top-6 +
 
 Timing: W eager warm-up steps, then the K timed steps are replayed from a
 captured HIP graph (per-call host overhead excluded, as in a captured decode
-loop); every step uses a different token and one of R address-distinct copies
-of the weights every step re-reads (router, shared expert), so the 256 MB
-Infinity Cache cannot serve them across steps.  A second, eager pass takes
-each kernel's start and end from HIP events recorded by its own launch
-(hipExtLaunchKernelGGL), the per-kernel durations used for the
-roofline entry.  The CPU oracle is then timed on a bounded sample of the same
-workload on the host cores.
+loop).  Every step takes a fresh batch of tokens and the next of R
+address-distinct copies of every weight tensor it reads (router, routed
+gate/up/down banks, shared expert), so the 256 MB Infinity Cache cannot carry
+weights from one step to the next.  The per-step spread (p10, median, p90)
+comes from one-step graphs replayed back to back with an event between
+replays.  An eager pass takes each kernel's start and end from HIP events
+recorded by its own launch (hipExtLaunchKernelGGL): the per-kernel durations
+used for the roofline entry.  A decode line also carries the prefill chunk's
+record (the MFMA half of the metric), measured the same way.  The CPU oracle
+is then timed on a bounded sample of the same workload on the host cores,
+once with all of them and once single-threaded.
 """
 import argparse
 import json
@@ -43,10 +47,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="decode_q8")
-    ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--replicas", type=int, default=8,
+                    help="address-distinct copies of every weight tensor, cycled step by step")
     ap.add_argument("--graph-steps", type=int, default=100)
+    ap.add_argument("--spread-steps", type=int, default=0,
+                    help="steps of the spread measurement (0: 200 for decode batches, 50 otherwise)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds-single", type=float, default=6.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-config", default="prefill",
+                    help="workload of the prefill sub-record carried by a decode line")
+    ap.add_argument("--no-prefill", action="store_true", help="omit the prefill sub-record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("PMC_FETCH", "PMC_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -299,6 +310,273 @@ def traffic_from(args):
     print(f"wrote {len(rows)} kernel(s) for {cfg_name} to {TRAFFIC_FILE}")
 
 
+def host_info():
+    """CPU model, visible cores and load average of the host running the bench."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        load = open("/proc/loadavg").read().split()[:3]
+    except OSError:
+        load = None
+    return {"cpu_model": model, "cpus_visible": os.cpu_count(), "loadavg": load}
+
+
+def gpu_clocks():
+    """Current shader (sclk) and memory (mclk) clocks in MHz, from the driver's
+    DPM tables in sysfs (the level marked '*'), else from rocm-smi; None when
+    neither is readable."""
+    import glob
+    import re
+    import subprocess
+    out = {}
+    for key in ("sclk", "mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{key}")):
+            try:
+                for line in open(path):
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                        if m:
+                            out[f"{key}_mhz"] = int(m.group(1))
+            except OSError:
+                continue
+            if f"{key}_mhz" in out:
+                break
+    if len(out) < 2:
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+            for key in ("sclk", "mclk"):
+                m = re.search(key + r"\s+clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", r.stdout, re.I)
+                if m and f"{key}_mhz" not in out:
+                    out[f"{key}_mhz"] = int(m.group(1))
+        except (OSError, subprocess.SubprocessError):
+            pass
+    return out or None
+
+
+def pct(v, q):
+    """q-th percentile (linear interpolation) of a list."""
+    v = sorted(v)
+    if not v:
+        return None
+    i = (len(v) - 1) * q / 100.0
+    lo, hi = int(math.floor(i)), int(math.ceil(i))
+    return v[lo] + (v[hi] - v[lo]) * (i - lo)
+
+
+def replicate_weights(qr, layer, R):
+    """R address-distinct copies of every weight tensor a step reads (router,
+    routed gate/up/down banks, shared expert) as moe_weights structs; copy 0 is
+    the layer's own.  Bias and hash table (a few KB per step) are shared."""
+    names = ("router_w", "gate", "up", "down", "sh_gate", "sh_up", "sh_down")
+    reps, keep = [], []
+    for r in range(R):
+        t = {n: getattr(layer, n) for n in names}
+        if r:
+            t = {n: (v.clone() if v is not None else None) for n, v in t.items()}
+        keep.append(t)
+
+        def p(v):
+            return None if v is None else v.data_ptr()
+        reps.append(qr.Weights(p(t["router_w"]), p(layer.router_b), p(layer.hash_table), p(t["gate"]), p(t["up"]),
+                               p(t["down"]), p(t["sh_gate"]), p(t["sh_up"]), p(t["sh_down"])))
+    return reps, keep
+
+
+def measure(cfg, K, W, G, R, spread_n, prof_n):
+    """Time one workload: W eager warm-up steps, K steps replayed from a graph
+    of G steps (each step a fresh batch of tokens and the next of R weight
+    copies), the per-step spread from about spread_n steps replayed as short
+    graphs bracketed by events, and prof_n eager steps with per-kernel events."""
+    import torch
+
+    import moe_synth as ms
+    import quantized_routed_moe_amd as qr
+
+    T, H, E, k, F = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn
+    dev = torch.device("cuda:0")
+    inp = ms.make_inputs(cfg)
+    layer = qr.MoELayer(H, E, k, F, cfg.shared, cfg.routed_fmt, cfg.route,
+                        cfg.vocab if cfg.route != "learned" else 0, table_k=cfg.table_k).load(inp)
+    wlist, keep = replicate_weights(qr, layer, R)
+    n_steps = W + G
+    xs = torch.from_numpy(ms.extra_tokens(cfg, n_steps * T)).to(dev).reshape(n_steps, T, H)
+    toks = None
+    if cfg.route != "learned":
+        toks = torch.from_numpy(ms.uniform_i32(n_steps * T, 0, cfg.vocab - 1, cfg.seed,
+                                               ms.TAG["token_ids"])).to(dev).reshape(n_steps, T)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = layer.ensure_workspace(T)
+
+    def step(i, stream=None):
+        qr.layer_forward(layer.shape, wlist[i % R], xs[i % n_steps], toks[i % n_steps] if toks is not None else None,
+                         out, ws, stream)
+
+    # distinct experts each step touches (for the algorithmic byte counts)
+    used = []
+    for i in range(n_steps):
+        r = layer.forward_debug(xs[i], toks[i] if toks is not None else None)
+        used.append(int(torch.count_nonzero(r["counts"]).item()))
+        del r
+    torch.cuda.synchronize()
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # G steps in one graph; a replay is checked bitwise against the eager call
+    gs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        for i in range(G):
+            step(W + i, torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    replay_out = out.clone()
+    step(W + G - 1)
+    torch.cuda.synchronize()
+    if not torch.equal(replay_out.view(torch.int32), out.view(torch.int32)):
+        raise RuntimeError("graph replay differs from the eager call")
+    replays = max(1, math.ceil(K / G))
+    K = replays * G
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+
+    # spread: graphs of S steps replayed back to back with an event between
+    # replays; a sample is one replay's time per step.  Decode batches take
+    # S = 10 (a graph launch leaves a gap of several microseconds on the GPU,
+    # which one-step graphs of a ~40 us step would count every time); longer
+    # steps take S = 1.
+    S = 10 if T <= 32 else 1
+    n_rep = max(1, spread_n // S)
+    sg = []
+    for j in range(min(n_rep, max(1, G // S))):
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=gs):
+            for i in range(S):
+                step(W + j * S + i, torch.cuda.current_stream())
+        sg.append(g1)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(n_rep):
+        sg[i % len(sg)].replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) / S for i in range(n_rep)]
+
+    # eager steps, host launch included; then eager steps with per-kernel events
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i % G)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / K
+    prof = qr.Profiler(max_events=16 * prof_n + 64)
+    prof.attach()
+    for i in range(prof_n):
+        step(W + i % G)
+    prof.detach()
+    torch.cuda.synchronize()
+    stages = prof.collect()
+    prof.close()
+    del graph, sg, keep
+    torch.cuda.empty_cache()
+    return {"inp": inp, "T": T, "K": K, "G": G, "ms_step": ms_step, "eager_ms": eager_ms, "spread_ms": per,
+            "spread_graph_steps": S,
+            "stages": stages, "prof_n": prof_n, "u_avg": u_avg_of(used, W, G, K)}
+
+
+def summarize(cfg, m):
+    """Stage table, roofline entry and layer fractions of one measurement."""
+    import quantized_routed_moe_amd as qr
+    model = stage_model(cfg, qr, m["u_avg"])
+    stages = m["stages"]
+    # a stage's time per call (all its launches) decides the dominant stage; its
+    # kernel's average launch duration prices the roofline entry
+    dom = max(stages, key=lambda s: stages[s][0])
+    dom_us = stages[dom][0] / stages[dom][1] * 1e3
+    roofline = make_roofline(cfg, model, dom, dom_us)
+    detail = {}
+    for s_, (ms_tot, n_) in stages.items():
+        us = ms_tot / m["prof_n"] * 1e3
+        b = model["stages"].get(s_, {}).get("bytes")
+        detail[s_] = {"us": round(us, 3), "launches": round(n_ / m["prof_n"], 2), "bytes": int(b) if b else None,
+                      "gbps": round(b / (us * 1e-6) / 1e9, 1) if b else None}
+    sec = m["ms_step"] * 1e-3
+    P = cfg.tokens * cfg.top_k + (cfg.tokens if cfg.shared else 0)
+    layer_ops = 2 * P * 3 * cfg.ffn * cfg.hidden
+    per = m["spread_ms"]
+    return {
+        "ms_per_step": round(m["ms_step"], 5),
+        "tokens_per_s": round(cfg.tokens / sec, 1),
+        "step_ms_p10_median_p90": [round(pct(per, q), 5) for q in (10, 50, 90)],
+        "spread": f"{len(per)} replays of {m['spread_graph_steps']}-step graphs, an event between replays; "
+                  "a sample is one replay's time per step",
+        "eager_ms_per_step": round(m["eager_ms"], 5),
+        "layer_bytes": int(model["layer_bytes"]),
+        "layer_gbps": round(model["layer_bytes"] / sec / 1e9, 1),
+        "layer_hbm_frac": round(model["layer_bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_int8_ops": int(layer_ops),
+        "layer_mfma_frac": round(layer_ops / sec / 1e12 / INT8_PEAK_TOPS, 4),
+        "distinct_experts_per_step": round(m["u_avg"], 2),
+        "stages": detail,
+        "roofline": roofline,
+        "model": model,
+    }
+
+
+def kernel_fracs(cfg, summ, stage):
+    """HBM, int8-MFMA and vector-ALU fractions of one stage's kernel."""
+    st = summ["model"]["stages"].get(stage)
+    us = summ["stages"].get(stage, {}).get("us")
+    if not st or not us:
+        return None
+    sec = us * 1e-6
+    kern = stage_kernel(cfg, stage)
+    e = {"kernel": kern, "us": us, "algorithmic_bytes": int(st["bytes"]),
+         "hbm_frac": round(st["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4)}
+    if st.get("ops"):
+        e["int8_ops"] = int(st["ops"])
+        e["mfma_frac"] = round(st["ops"] / sec / 1e12 / INT8_PEAK_TOPS, 4)
+        e["alu_frac"] = round(st["valu"] / sec / 1e12 / VALU_PEAK_TOPS, 4)
+    e["traffic"] = stored_traffic(cfg, kern)
+    return e
+
+
+def cpu_baseline(cfg, inp, seconds, threads):
+    """The oracle as it stands, timed on the host on fresh tokens of the same
+    workload: batches of `threads` tokens (OpenMP over tokens) until about
+    `seconds` of compute."""
+    import moe_synth as ms
+    import oracle
+    used = oracle.set_threads(threads)
+    T = cfg.tokens
+    n_host = max(4096, 64 * T)
+    xs_host = ms.extra_tokens(cfg, n_host)
+    tk_host = (ms.uniform_i32(n_host, 0, cfg.vocab - 1, cfg.seed, ms.TAG["token_ids"])
+               if cfg.route != "learned" else None)
+    n_tok, spent, batch = 0, 0.0, max(used, 1)
+    while spent < seconds and n_tok + batch <= xs_host.shape[0]:
+        sel = slice(n_tok, n_tok + batch)
+        t0 = time.perf_counter()
+        oracle.forward(cfg, inp, x=xs_host[sel], token_ids=tk_host[sel] if tk_host is not None else None, want=False)
+        spent += time.perf_counter() - t0
+        n_tok += batch
+    return {"value": round(n_tok / spent, 3) if spent > 0 else None, "unit": "tokens/s", "cores": used,
+            "sample": f"{n_tok} tokens of the same workload, {batch} per oracle call, {spent:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -313,115 +591,29 @@ def main():
         traffic_from(args)
         return
 
-    import numpy as np
     import torch
 
     import moe_synth as ms
-    import quantized_routed_moe_amd as qr
 
     cfg = ms.CONFIGS[args.config]
     T, H, E, k, F = cfg.tokens, cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn
-    fmt = qr.FMT[cfg.routed_fmt]
     torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
+    host = host_info()
     t_setup = time.time()
-    inp = ms.make_inputs(cfg)
-    layer = qr.MoELayer(H, E, k, F, cfg.shared, cfg.routed_fmt, cfg.route,
-                        cfg.vocab if cfg.route != "learned" else 0, table_k=cfg.table_k).load(inp)
     R = max(1, args.replicas)
-    reps = []
-    for r in range(R):
-        if r == 0:
-            reps.append((layer.router_w, (layer.sh_gate, layer.sh_up, layer.sh_down)))
-        else:
-            rw = layer.router_w.clone() if layer.router_w is not None else None
-            reps.append((rw, (layer.sh_gate.clone(), layer.sh_up.clone(), layer.sh_down.clone())))
-    wlist = [layer.weights(router_w=rw, sh=sh) for rw, sh in reps]
     G = max(1, min(args.graph_steps, args.steps))
-    n_steps = args.warmup + G
-    xs = torch.from_numpy(ms.extra_tokens(cfg, n_steps * T)).to(dev).reshape(n_steps, T, H)
-    toks = None
-    if cfg.route != "learned":
-        toks = torch.from_numpy(ms.uniform_i32(n_steps * T, 0, cfg.vocab - 1, cfg.seed,
-                                               ms.TAG["token_ids"])).to(dev).reshape(n_steps, T)
-    out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws = layer.ensure_workspace(T)
-
-    def step(i, stream=None):
-        qr.layer_forward(layer.shape, wlist[i % R], xs[i], toks[i] if toks is not None else None, out, ws, stream)
-
-    # distinct experts each step touches (for the algorithmic byte counts)
-    used = []
-    for i in range(n_steps):
-        r = layer.forward_debug(xs[i], toks[i] if toks is not None else None)
-        used.append(int(torch.count_nonzero(r["counts"]).item()))
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # capture G steps in one graph, check a replay against eager, then time K steps of replays
-    gs = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=gs):
-        for i in range(G):
-            step(args.warmup + i, torch.cuda.current_stream())
-    graph.replay()
-    torch.cuda.synchronize()
-    replay_out = out.clone()
-    step(args.warmup + G - 1)
-    torch.cuda.synchronize()
-    if not torch.equal(replay_out.view(torch.int32), out.view(torch.int32)):
-        raise RuntimeError("graph replay differs from the eager call")
-    replays = max(1, math.ceil(args.steps / G))
-    K = replays * G
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(replays):
-        graph.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    value = K * T / (t1 - t0)
-
-    # eager region (host launch overhead included), then eager with per-kernel events
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(args.warmup + i % G)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / K
-    KP = min(K, 300)
-    prof = qr.Profiler(max_events=8 * KP + 64)
-    prof.attach()
-    for i in range(KP):
-        step(args.warmup + i % G)
-    prof.detach()
-    torch.cuda.synchronize()
-    stages = prof.collect()
-    prof.close()
-
-    model = stage_model(cfg, qr, u_avg_of(used, args.warmup, G, K))
-    dom = max(stages, key=lambda s: stages[s][0])
-    dom_us = stages[dom][0] / stages[dom][1] * 1e3
-    roofline = make_roofline(cfg, model, dom, dom_us)
-    layer_bytes = model["layer_bytes"]
-    stage_detail = {}
-    for s_, (ms_tot, n_) in stages.items():
-        us = ms_tot / n_ * 1e3
-        b = model["stages"].get(s_, {}).get("bytes")
-        stage_detail[s_] = {"us": round(us, 3), "bytes": int(b) if b else None,
-                            "gbps": round(b / (us * 1e-6) / 1e9, 1) if b else None}
-
+    spread_n = args.spread_steps or (200 if T <= 32 else 50)
+    m = measure(cfg, args.steps, args.warmup, G, R, spread_n, min(args.steps, 300))
+    summ = summarize(cfg, m)
+    K = m["K"]
     res = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": summ["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": summ["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -434,39 +626,53 @@ def main():
             "tokens_per_step": T,
             "parallelism": "single GPU",
             "weight_replicas": R,
-            "timing": f"HIP-graph replay of {G}-step graphs",
+            "timing": f"HIP-graph replay of {G}-step graphs; every step a fresh batch and the next of {R} "
+                      "address-distinct copies of all weights (router, routed banks, shared expert)",
         },
-        "layer_gbps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "layer_hbm_frac": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "eager_ms_per_step": round(eager_ms, 5),
-        "stages": stage_detail,
-        "roofline": roofline,
+        "step_ms_p10_median_p90": summ["step_ms_p10_median_p90"],
+        "spread": summ["spread"],
+        "layer_gbps": summ["layer_gbps"],
+        "layer_hbm_frac": summ["layer_hbm_frac"],
+        "eager_ms_per_step": summ["eager_ms_per_step"],
+        "distinct_experts_per_step": summ["distinct_experts_per_step"],
+        "stages": summ["stages"],
+        "roofline": summ["roofline"],
         "cpu_baseline": None,
-        "setup_s": round(time.time() - t_setup, 1),
+        "host": host,
+        "gpu_clocks": None,
     }
+    inp = m.pop("inp")
+    res["gpu_clocks"] = gpu_clocks()
+
+    if not args.no_prefill and T <= 32:
+        # the prefill half of the metric: MFMA utilisation of the chunk
+        del inp
+        pcfg = ms.CONFIGS[args.prefill_config]
+        pm = measure(pcfg, 20, 3, 10, R, 50, 20)
+        pm.pop("inp")
+        ps = summarize(pcfg, pm)
+        res["prefill"] = {
+            "workload": f"{pcfg.name}: {pcfg.tokens} tokens/step, hidden {pcfg.hidden}, {pcfg.n_experts} experts "
+                        f"top-{pcfg.top_k} + 1 shared, FFN {pcfg.ffn}, routed {pcfg.routed_fmt.upper()}, "
+                        f"{pcfg.route} routing",
+            "steps": pm["K"],
+            **{key: ps[key] for key in ("ms_per_step", "tokens_per_s", "step_ms_p10_median_p90", "layer_bytes",
+                                        "layer_gbps", "layer_hbm_frac", "layer_int8_ops", "layer_mfma_frac",
+                                        "distinct_experts_per_step")},
+            "gateup_mfma": kernel_fracs(pcfg, ps, "gateup"),
+            "down_mfma": kernel_fracs(pcfg, ps, "down"),
+            "stages": ps["stages"],
+        }
+        inp = None
 
     if not args.no_cpu_baseline:
-        import oracle
-        threads = oracle.set_threads(0)
-        n_host = max(4096, 64 * T)
-        xs_host = ms.extra_tokens(cfg, n_host)
-        tk_host = (ms.uniform_i32(n_host, 0, cfg.vocab - 1, cfg.seed, ms.TAG["token_ids"])
-                   if cfg.route != "learned" else None)
-        n_tok, spent, batch = 0, 0.0, max(threads, 1)
-        while spent < args.cpu_seconds and n_tok + batch <= xs_host.shape[0]:
-            sel = slice(n_tok, n_tok + batch)
-            t0 = time.perf_counter()
-            oracle.forward(cfg, inp, x=xs_host[sel], token_ids=tk_host[sel] if tk_host is not None else None,
-                           want=False)
-            spent += time.perf_counter() - t0
-            n_tok += batch
-        res["cpu_baseline"] = {
-            "value": round(n_tok / spent, 3) if spent > 0 else None,
-            "unit": "tokens/s",
-            "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n_tok} tokens of the same workload, {batch} per oracle call, {spent:.1f} s",
-        }
+        if inp is None:
+            inp = ms.make_inputs(cfg)
+        multi = cpu_baseline(cfg, inp, args.cpu_seconds, 0)
+        single = cpu_baseline(cfg, inp, args.cpu_seconds_single, 1)
+        res["cpu_baseline"] = {**multi, "kind": "oracle", "single_thread": single}
+    res["host"]["loadavg_end"] = host_info()["loadavg"]
+    res["setup_s"] = round(time.time() - t_setup, 1)
     print(json.dumps(res), flush=True)
 
 
