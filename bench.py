@@ -482,7 +482,7 @@ def measure(cfg, K, W, G, R, spread_n, prof_n):
         step(W + i % G)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / K
-    prof = qr.Profiler(max_events=16 * prof_n + 64)
+    prof = qr.Profiler(max_events=24 * prof_n + 64)  # up to 12 launches per step, 2 events each
     prof.attach()
     for i in range(prof_n):
         step(W + i % G)
