@@ -352,18 +352,22 @@ __global__ __launch_bounds__(512) void decode_gateup1_kernel(LayerArgs a) {
 // routed format's geometry; the shared Q8 expert reuses it with more chunks
 // per lane).  Every selected expert's row is requested before h is staged.
 constexpr int kMaxSel = kMaxSelList;  // top_k <= 8 plus the shared expert
+constexpr int kD1Waves = 8;           // waves of a one-token down workgroup (they share the staged h)
 
 // NR routed row slots per lane (top_k <= NR); every slot is loaded and
 // reduced, the ones past the routed groups are dropped at the combine.
 template <int F, int FMT, bool DUMP, int NR>
-__global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
+// (4096-wide Q8 rows hold 4 chunks a lane per expert: those run at 2 waves per SIMD)
+__global__ __launch_bounds__(64 * kD1Waves, (F == 4096 && FMT == kFmtQ8) ? 2 : 4) void decode_down1_kernel(LayerArgs a) {
     constexpr int L = DefLpr<F, FMT>::v;
     constexpr int RPW = 64 / L;
-    constexpr int NS = (kMaxSel * (F / 32) + 255) / 256;  // h block scales per thread
+    constexpr int NT = 64 * kD1Waves;
+    constexpr int NS = ((NR + 1) * (F / 32) + NT - 1) / NT;  // h block scales per thread (G <= NR + 1)
+    constexpr int NH = ((NR + 1) * (F / 16) + NT - 1) / NT;  // 16-byte h code chunks per thread
     __shared__ VecSmem<F, kMaxSel> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Dims &d = a.d;
-    const int seg = lane % L, r = (blockIdx.x * 4 + wave) * RPW + lane / L;
+    const int seg = lane % L, r = (blockIdx.x * kD1Waves + wave) * RPW + lane / L;
     // Loads are issued in the order their results are needed, because a wave
     // waits for loads in issue order: the shared expert's row (needs no
     // routing), the work list, the h rows and combine weights of the groups,
@@ -393,24 +397,28 @@ __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
     float hdv[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        const int idx = tid + 256 * u;
+        const int idx = tid + NT * u;
         const bool ok = idx < G * (F / 32);
         QRMOE_PAIR_OF(p, ok ? idx / (F / 32) : 0);
         hdv[u] = a.ws.hd[(int64_t)p * (F / 32) + (ok ? idx % (F / 32) : 0)];
     }
-    // h codes of the G pairs go straight to LDS (aq rows are contiguous): one
-    // 1 KB global->LDS load per wave instruction, each lane 16 bytes of its own
-    // pair's row; G*F is a multiple of 1 KB for F >= 1024
-    if constexpr (F >= 1024) {
-        const int ninst = G * F / 1024;
-        for (int j = wave; j < ninst; j += 4) {
-            const int o = j * 1024 + lane * 16;
-            QRMOE_PAIR_OF(p, o / F);
-            __builtin_amdgcn_global_load_lds(a.ws.hq + (int64_t)p * F + o % F,
-                                             (lds_ptr)(&sm.aq[0][0] + j * 1024), 16, 0, 0);
-        }
+    // h codes of the G pairs: loads now (in registers), LDS after the rows
+    // are requested, so the wave waits for h and then for each row in turn
+    // instead of for all of them at once.  Chunks past the G pairs re-read
+    // pair 0's row and are not stored.
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    v4i hv[NH];
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+        const int idx = tid + NT * u;
+        const bool ok = idx < G * (F / 16);
+        QRMOE_PAIR_OF(p, ok ? idx / (F / 16) : 0);
+        hv[u] = reinterpret_cast<const v4i *>(a.ws.hq + (int64_t)p * F)[ok ? idx % (F / 16) : 0];
     }
 #undef QRMOE_PAIR_OF
+    // The compiler may not move the loads above below the rows (a wave's loads
+    // return in issue order, so each would then wait for every row).
+    __builtin_amdgcn_sched_barrier(0);
     // Every slot loads without a branch (a slot past the routed groups re-reads
     // group 0's row, served by the cache), so nothing is sunk below the rows.
     const int64_t mb = mat_bytes(FMT, d.H, F);
@@ -423,25 +431,31 @@ __global__ __launch_bounds__(256) void decode_down1_kernel(LayerArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        const int idx = tid + 256 * u;
+        const int idx = tid + NT * u;
         if (idx < G * (F / 32)) sm.ad[idx / (F / 32)][idx % (F / 32)] = hdv[u];
     }
-    if constexpr (F < 1024) {
-        for (int i = tid; i < G * (F / 16); i += 256) {
-            const int tok = i / (F / 16);
-            int p = gp[0];
+    // Every thread stores each chunk it loaded (chunks past the G pairs go to
+    // a junk slot in the h area, which this kernel does not use otherwise):
+    // a store under a branch would let the compiler sink its load below the
+    // rows.  2-bit weights also need h's 16-code subblock sums: a chunk is
+    // one subblock.
+    v4i *junk = reinterpret_cast<v4i *>(&sm.h[0][0]) + (tid & 127);
+    static_assert(sizeof(sm.h) >= 128 * sizeof(v4i), "junk slots");
 #pragma unroll
-            for (int jj = 1; jj < kMaxSel; ++jj) p = tok == jj ? gp[jj] : p;
-            reinterpret_cast<int4 *>(sm.aq[tok])[i % (F / 16)] =
-                reinterpret_cast<const int4 *>(a.ws.hq + (int64_t)p * F)[i % (F / 16)];
+    for (int u = 0; u < NH; ++u) {
+        const int idx = tid + NT * u;
+        const bool ok = idx < G * (F / 16);
+        v4i *dst = ok ? reinterpret_cast<v4i *>(sm.aq[idx / (F / 16)]) + idx % (F / 16) : junk;
+        *dst = hv[u];
+        if constexpr (FMT == kFmtQ2) {
+            int sub = sdot4(hv[u][0], 0x01010101, 0);
+            sub = sdot4(hv[u][1], 0x01010101, sub);
+            sub = sdot4(hv[u][2], 0x01010101, sub);
+            sub = sdot4(hv[u][3], 0x01010101, sub);
+            if (ok) sm.as16[idx / (F / 16)][idx % (F / 16)] = sub;
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's global->LDS loads have landed (the rows too)
     __syncthreads();
-    if constexpr (FMT == kFmtQ2) {
-        subblock_sums(sm, G);
-        __syncthreads();
-    }
     // Same arithmetic per expert as the batched down + combine: y = w * (sum
     // over lanes), summed in ascending expert id, the shared expert last.
     // The shared expert's row was requested first, so it is reduced first.
@@ -542,7 +556,7 @@ hipError_t launch_decode_gateup1(const LayerArgs &a, bool dump, hipStream_t s) {
 template <int F, int FMT, bool DUMP>
 static hipError_t down1_h(const LayerArgs &a, hipStream_t s) {
     constexpr int RPW = 64 / DefLpr<F, FMT>::v;
-    const dim3 grid(a.d.H / (4 * RPW)), block(256);
+    const dim3 grid(a.d.H / (kD1Waves * RPW)), block(64 * kD1Waves);
     if (a.d.k <= 2) klaunch(decode_down1_kernel<F, FMT, DUMP, 2>, grid, block, s, a);
     else if (a.d.k <= 6) klaunch(decode_down1_kernel<F, FMT, DUMP, 6>, grid, block, s, a);
     else klaunch(decode_down1_kernel<F, FMT, DUMP, kMaxSel - 1>, grid, block, s, a);
