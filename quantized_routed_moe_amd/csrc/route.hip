@@ -188,37 +188,46 @@ hipError_t launch_quant(const LayerArgs &a, hipStream_t s) {
 // Tiled logits: a workgroup computes a 32-token x 32-expert tile, each thread
 // 2 tokens x 2 experts.  The H-long sum is the adjacent-pair tree of the
 // exact fp64 products:
-//  - chunks of 64 elements of the tile's x and W rows are staged in LDS as
-//    fp32 (fp64 rows would double the LDS traffic per product, which then
-//    bounds the kernel); the next chunk's global loads are in flight while
-//    the current one is reduced;
+//  - chunks of 128 elements of the tile's x and W rows are staged in LDS
+//    (x as fp64, W as fp32, see below); the next chunk's global loads are in
+//    flight while the current one is reduced;
 //  - each 8-element run gives a level-3 node in registers, its level-1 nodes
 //    as fma(x1, w1, x0 * w0) (both products are exact in fp64, so this
-//    rounds exactly like the sum of the two products); the chunk's 8 runs
-//    combine into its level-6 node by a compile-time tree;
+//    rounds exactly like the sum of the two products); the chunk's 16 runs
+//    combine into its level-7 node by a compile-time tree;
 //  - the chunk nodes are merged by a binary counter: after chunk c, merge
 //    with the stacked left siblings once per trailing one bit of c.  With
-//    2^m chunks this is exactly the adjacent-pair tree; the merges are
-//    uniform branches, no dynamic indexing.
+//    2^m chunks this is exactly the adjacent-pair tree.  The merges are
+//    selects on every level, so fewer, longer chunks cost fewer of them
+//    (and fewer barriers): 128-element chunks took the 2048-token router
+//    from 216 to 200 us against 64-element ones.
 constexpr int kLogTile = 32;
-constexpr int kLogChunk = 64;
+constexpr int kLogChunk = 128;
 constexpr int kLogRun = 8;      // elements per register subtree (a level-3 node)
-constexpr int kLogLevels = 7;   // stack levels: up to 2^6 chunks, H <= 4096
+constexpr int kLogLevels = 6;   // stack levels: up to 2^5 chunks, H <= 4096
 constexpr int kLogPad = 4;      // row padding (keeps 16-byte rows aligned)
 
+// x rows are staged already converted to fp64 (each x element meets 32 W
+// rows, so converting it once saves half the conversions; every lane group of
+// 16 reads the same x row, so the wider rows cost little LDS bandwidth).  W
+// rows stay fp32: a wave reads 16 different W rows, and as fp64 they would
+// double the LDS bytes of the operand that is not broadcast.
 struct LogitsSmem {
-    alignas(16) float xs[kLogTile][kLogChunk + kLogPad];
+    alignas(16) double xs[kLogTile][kLogChunk + kLogPad / 2];
     alignas(16) float wsm[kLogTile][kLogChunk + kLogPad];
 };
 
-// One thread's share of a chunk in registers: 2 float4 of x rows, 2 of W rows.
+// One thread's share of a chunk in registers: NV float4 of x rows and NV of
+// W rows (32 rows of kLogChunk elements each, 16-byte pieces).
 struct LogitChunkRegs {
-    float4 x[2], w[2];
+    static constexpr int NV = kLogTile * kLogChunk / 4 / 256;
+    static constexpr int PR = kLogChunk / 4;  // pieces per row
+    float4 x[NV], w[NV];
     __device__ __forceinline__ void load(const float *__restrict__ x0, const float *__restrict__ w0, int H, int T,
                                          int E, int tb, int eb, int c) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = threadIdx.x + 256 * i, row = idx >> 4, col = (idx & 15) * 4;
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + 256 * i, row = idx / PR, col = (idx % PR) * 4;
             const int t = tb + row, e = eb + row;
             // rows past T / E read row 0 of the tile and are zeroed at the store
             x[i] = *reinterpret_cast<const float4 *>(x0 + (int64_t)(t < T ? t : tb) * H + c * kLogChunk + col);
@@ -231,29 +240,33 @@ struct LogitChunkRegs {
     }
     __device__ __forceinline__ void store(LogitsSmem &sm, int T, int E, int tb, int eb) const {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = threadIdx.x + 256 * i, row = idx >> 4, col = (idx & 15) * 4;
-            *reinterpret_cast<float4 *>(&sm.xs[row][col]) = keep(tb + row < T, x[i]);
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + 256 * i, row = idx / PR, col = (idx % PR) * 4;
+            const float4 xv = keep(tb + row < T, x[i]);
+            *reinterpret_cast<double2 *>(&sm.xs[row][col]) = make_double2((double)xv.x, (double)xv.y);
+            *reinterpret_cast<double2 *>(&sm.xs[row][col + 2]) = make_double2((double)xv.z, (double)xv.w);
             *reinterpret_cast<float4 *>(&sm.wsm[row][col]) = keep(eb + row < E, w[i]);
         }
     }
 };
 
 // Level-3 nodes of the 4 (token, expert) pairs of this thread over the run
-// of 8 elements at i0 of the staged chunk (each element converted to fp64
-// where it is used).
+// of 8 elements at i0 of the staged chunk (W elements converted to fp64
+// where they are used).
 __device__ __forceinline__ void logit_run(const LogitsSmem &sm, int t0, int e0, int i0, double r[4]) {
-    float xa[2][kLogRun], wa[2][kLogRun];
+    double xa[2][kLogRun];
+    float wa[2][kLogRun];
 #pragma unroll
     for (int q = 0; q < kLogRun; q += 4) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const float4 xv = *reinterpret_cast<const float4 *>(&sm.xs[t0 + 16 * k][i0 + q]);
+            const double2 x01 = *reinterpret_cast<const double2 *>(&sm.xs[t0 + 16 * k][i0 + q]);
+            const double2 x23 = *reinterpret_cast<const double2 *>(&sm.xs[t0 + 16 * k][i0 + q + 2]);
             const float4 wv = *reinterpret_cast<const float4 *>(&sm.wsm[e0 + 16 * k][i0 + q]);
-            xa[k][q] = xv.x;
-            xa[k][q + 1] = xv.y;
-            xa[k][q + 2] = xv.z;
-            xa[k][q + 3] = xv.w;
+            xa[k][q] = x01.x;
+            xa[k][q + 1] = x01.y;
+            xa[k][q + 2] = x23.x;
+            xa[k][q + 3] = x23.y;
             wa[k][q] = wv.x;
             wa[k][q + 1] = wv.y;
             wa[k][q + 2] = wv.z;
@@ -267,8 +280,8 @@ __device__ __forceinline__ void logit_run(const LogitsSmem &sm, int t0, int e0, 
             double n1[kLogRun / 2];
 #pragma unroll
             for (int j = 0; j < kLogRun / 2; ++j)
-                n1[j] = __fma_rn((double)xa[ti][2 * j + 1], (double)wa[ei][2 * j + 1],
-                                 __dmul_rn((double)xa[ti][2 * j], (double)wa[ei][2 * j]));
+                n1[j] = __fma_rn(xa[ti][2 * j + 1], (double)wa[ei][2 * j + 1],
+                                 __dmul_rn(xa[ti][2 * j], (double)wa[ei][2 * j]));
             r[ti * 2 + ei] = __dadd_rn(__dadd_rn(n1[0], n1[1]), __dadd_rn(n1[2], n1[3]));
         }
 }
@@ -320,7 +333,7 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(LayerArgs a) {
                 for (int i = 0; i < 4; ++i) st[l][i] = v[i];
     }
     int top = 0;
-    while ((kLogChunk << top) < H) ++top;  // H / 64 = 2^top chunks: the total sits at level top
+    while ((kLogChunk << top) < H) ++top;  // H / 128 = 2^top chunks: the total sits at level top
     double r[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int l = 0; l < kLogLevels; ++l)
