@@ -208,7 +208,10 @@ int forward_impl(const moe_shape *shape, const moe_weights *wts, const float *x,
     a.d = Dims{(int32_t)T, shape->hidden, shape->n_experts, shape->top_k, shape->ffn, shape->has_shared,
                shape->routed_fmt, shape->route, shape->vocab,
                (int32_t)(T * shape->top_k + (shape->has_shared ? T : 0)),
-               hashed && shape->table_k ? shape->table_k : shape->top_k};
+               hashed && shape->table_k ? shape->table_k : shape->top_k,
+               // the score-weighted hash reads only the scores of its table's
+               // experts; the debug call copies every logit, so it computes all
+               (int32_t)(shape->route == MOE_ROUTE_HASH_SCORED && !dbg)};
     a.wt = Weights{wts->router_w, wts->router_b, wts->hash_table, (const uint8_t *)wts->gate,
                    (const uint8_t *)wts->up, (const uint8_t *)wts->down, (const uint8_t *)wts->sh_gate,
                    (const uint8_t *)wts->sh_up, (const uint8_t *)wts->sh_down};

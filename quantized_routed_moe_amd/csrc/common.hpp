@@ -47,6 +47,7 @@ struct Dims {
     int32_t T, H, E, k, F, has_shared, fmt, route, vocab;
     int32_t P;  // pairs including the shared expert's: T*k + T*has_shared
     int32_t table_k;  // entries per hash-table row (>= k)
+    int32_t table_logits;  // score-weighted hash, decode sizes, no debug copies: only the table's logits
 };
 
 // Workspace pointers (device).

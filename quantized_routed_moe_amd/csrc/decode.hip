@@ -30,12 +30,28 @@ __global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_le
     for (int b = blockIdx.x * 256 + tid; b < nblk; b += n_lead * 256)
         quant_one_block(a.x, a.ws.xq, a.ws.xd, d.fmt == kFmtQ2 ? a.ws.xs16 : nullptr, b);
     if (d.route == kRouteHash) return;  // no router
-    const int nlog = d.T * d.E;
+    // every (token, expert) logit, or with table_logits the (token, entry j)
+    // ones of the table's first k entries (clamped as the selection clamps
+    // them; an expert named twice is computed twice, with the same bits)
+    const int nlog = d.table_logits ? d.T * d.k : d.T * d.E;
+    auto pair_of = [&](int le, int &t, int &e) {
+        if (d.table_logits) {
+            t = le / d.k;
+            int id = a.token_ids[t];
+            if (id < 0 || id >= d.vocab) id = 0;
+            e = a.wt.table[(int64_t)id * d.table_k + le % d.k];
+            if (e < 0 || e >= d.E) e = 0;
+        } else {
+            t = le / d.E;
+            e = le % d.E;
+        }
+    };
     if constexpr (H >= 256) {
         // one logit per workgroup; wave w sums elements [w*H/4, (w+1)*H/4)
         constexpr int SEG = H / 256;
         for (int le = blockIdx.x; le < nlog; le += n_lead) {
-            const int t = le / d.E, e = le % d.E;
+            int t, e;
+            pair_of(le, t, e);
             const int off = wave * (H / 4) + lane * SEG;
             const double v =
                 wave_sum_f64(segment_tree<SEG>(a.x + (int64_t)t * H + off, a.wt.router_w + (int64_t)e * H + off));
@@ -43,18 +59,21 @@ __global__ __launch_bounds__(256) void decode_front_kernel(LayerArgs a, int n_le
             __syncthreads();
             if (tid == 0) {
                 const float l = (float)((part[0] + part[1]) + (part[2] + part[3]));
-                a.ws.logits[le] = l;
-                score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
+                const int64_t i = (int64_t)t * d.E + e;
+                a.ws.logits[i] = l;
+                score_key(l, a.wt.router_b, e, a.ws.scores + i, a.ws.keys + i);
             }
             __syncthreads();
         }
     } else {
         for (int le = blockIdx.x * 4 + wave; le < nlog; le += n_lead * 4) {
-            const int t = le / d.E, e = le % d.E;
+            int t, e;
+            pair_of(le, t, e);
             const float l = wave_logit<H>(a.x + (int64_t)t * H, a.wt.router_w + (int64_t)e * H, lane);
             if (lane == 0) {
-                a.ws.logits[le] = l;
-                score_key(l, a.wt.router_b, e, a.ws.scores + le, a.ws.keys + le);
+                const int64_t i = (int64_t)t * d.E + e;
+                a.ws.logits[i] = l;
+                score_key(l, a.wt.router_b, e, a.ws.scores + i, a.ws.keys + i);
             }
         }
     }
@@ -492,7 +511,8 @@ static hipError_t front_h(const LayerArgs &a, hipStream_t s) {
     const int nq = (d.T * (H / 32) + 255) / 256;
     int n_lead = nq;
     if (d.route != kRouteHash) {
-        const int nl = H >= 256 ? d.T * d.E : (d.T * d.E + 3) / 4;
+        const int n = d.table_logits ? d.T * d.k : d.T * d.E;
+        const int nl = H >= 256 ? n : (n + 3) / 4;
         n_lead = nl > nq ? nl : nq;
     }
     if (n_lead > 4096) n_lead = 4096;

@@ -452,6 +452,35 @@ def test_repeated_expert_flag_each_selection_path(T):
     assert layer.flags() == qr.FLAG_REPEATED_EXPERT
 
 
+@pytest.mark.parametrize("T", [1, 5])
+def test_score_weighted_hash_clamps_like_the_selection(T):
+    """Score-weighted hash with an out-of-range token id and a table entry out
+    of range (an unchecked table): the product call, whose router computes
+    only the logits of the table's experts, clamps both as the selection does
+    and equals the debug call (every logit computed) bit for bit; both
+    conditions are flagged."""
+    qr = _qr()
+    cfg = ms.LayerConfig(f"hash_scored_clamp_T{T}", 512, 32, 4, 256, T, route="hash_scored", vocab=50,
+                         seed=60 + T)
+    inp = ms.make_inputs(cfg)
+    inp["hash_table"][7] = np.array([3, 40, 9, 1], dtype=np.int32)  # expert 40 >= 32 experts
+    layer = qr.MoELayer(512, 32, 4, 256, True, "q8", "hash_scored", 50).load(inp)
+    tok = inp["token_ids"].copy()
+    tok[0] = 7
+    if T > 1:
+        tok[T - 1] = 50  # token id >= vocab
+    x = torch.from_numpy(inp["x"]).cuda()
+    tt = torch.from_numpy(tok).cuda()
+    r = layer.forward_debug(x, tt)
+    plain = layer.forward(x, tt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(plain).all()
+    assert torch.equal(plain.view(torch.int32), r["out"].view(torch.int32))
+    assert layer.flags() & qr.FLAG_BAD_TABLE_ENTRY
+    if T > 1:
+        assert layer.flags() & qr.FLAG_BAD_TOKEN
+
+
 def test_check_hash_table():
     qr = _qr()
     cfg = ms.LayerConfig("table", 256, 16, 2, 128, 4, route="hash", vocab=1000, seed=34)
