@@ -102,10 +102,44 @@ def _check(status: int, what: str):
         raise MoEError(status, what)
 
 
-def _ptr(t):
+def _layout(t, name, dtype=None, shape=None):
+    """The checks the C ABI cannot make on a plain pointer: the shape and
+    dtype it assumes and a dense layout."""
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _on_gpu(t, name):
+    """Device pointer of t; a host pointer handed to the kernels would fault."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be in GPU memory")
     return t.data_ptr()
+
+
+def _dev(t, name, dtype=None, shape=None):
+    _layout(t, name, dtype, shape)
+    return _on_gpu(t, name)
+
+
+def _batch(shape, x, token_ids, out):
+    """Checked pointers of one forward call's x [T, H] fp32, token_ids [T]
+    int32 (hash routes) and out [T, H] fp32; returns (T, x, tokens, out)."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError(f"x: expected [tokens, {shape.hidden}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    _layout(x, "x", torch.float32, (T, shape.hidden))
+    _layout(token_ids, "token_ids", torch.int32, (T,))
+    _layout(out, "out", torch.float32, (T, shape.hidden))
+    return T, _on_gpu(x, "x"), _on_gpu(token_ids, "token_ids"), _on_gpu(out, "out")
 
 
 def _stream(stream=None):
@@ -133,17 +167,18 @@ def workspace_bytes(shape: Shape, tokens: int) -> int:
 
 
 def pack_weights(fmt: int, canonical, packed, n_mats: int, rows: int, cols: int, stream=None):
-    _check(_lib.moe_pack_weights(fmt, _ptr(canonical), _ptr(packed), n_mats, rows, cols, _stream(stream)),
-           "moe_pack_weights")
+    _check(_lib.moe_pack_weights(fmt, _dev(canonical, "canonical"), _dev(packed, "packed"), n_mats, rows, cols,
+                                 _stream(stream)), "moe_pack_weights")
 
 
 def workspace_init(ws, stream=None):
-    _check(_lib.moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_workspace_init")
+    _check(_lib.moe_workspace_init(_dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_workspace_init")
 
 
 def workspace_flags(ws, stream=None) -> int:
     f = _I32(0)
-    _check(_lib.moe_workspace_flags(_ptr(ws), ctypes.byref(f), _stream(stream)), "moe_workspace_flags")
+    _check(_lib.moe_workspace_flags(_dev(ws, "workspace"), ctypes.byref(f), _stream(stream)), "moe_workspace_flags")
     return f.value
 
 
@@ -151,31 +186,33 @@ def check_hash_table(table, n_experts: int, ws, stream=None) -> int:
     """-1 when the table is valid; raises MoEError(BAD_TABLE) naming the first bad row otherwise."""
     bad = _I32(-1)
     vocab, k = table.shape
-    st = _lib.moe_check_hash_table(_ptr(table), vocab, k, n_experts, _ptr(ws), ws.numel() * ws.element_size(),
-                                   ctypes.byref(bad), _stream(stream))
+    import torch
+    st = _lib.moe_check_hash_table(_dev(table, "table", torch.int32), vocab, k, n_experts, _dev(ws, "workspace"),
+                                   ws.numel() * ws.element_size(), ctypes.byref(bad), _stream(stream))
     if st != 0:
         raise MoEError(st, f"moe_check_hash_table (first bad row {bad.value})")
     return bad.value
 
 
 def layer_forward(shape: Shape, weights: Weights, x, token_ids, out, ws, stream=None, debug: Debug | None = None):
-    T = x.shape[0] if x.dim() == 2 else 0
+    T, px, pt, po = _batch(shape, x, token_ids, out)
+    pw = _dev(ws, "workspace")
     nbytes = ws.numel() * ws.element_size()
     if debug is None:
-        st = _lib.moe_layer_forward(ctypes.byref(shape), ctypes.byref(weights), _ptr(x), _ptr(token_ids), T,
-                                    _ptr(out), _ptr(ws), nbytes, _stream(stream))
+        st = _lib.moe_layer_forward(ctypes.byref(shape), ctypes.byref(weights), px, pt, T, po, pw, nbytes,
+                                    _stream(stream))
     else:
-        st = _lib.moe_layer_forward_debug(ctypes.byref(shape), ctypes.byref(weights), _ptr(x), _ptr(token_ids), T,
-                                          _ptr(out), _ptr(ws), nbytes, ctypes.byref(debug), _stream(stream))
+        st = _lib.moe_layer_forward_debug(ctypes.byref(shape), ctypes.byref(weights), px, pt, T, po, pw, nbytes,
+                                          ctypes.byref(debug), _stream(stream))
     _check(st, "moe_layer_forward")
     return out
 
 
 def layer_forward_static(shape: Shape, weights: Weights, x, token_ids, out, stream=None):
     """moe_layer_forward_static: the layer on the library's per-GPU scratch array (allocates nothing)."""
-    T = x.shape[0] if x.dim() == 2 else 0
-    _check(_lib.moe_layer_forward_static(ctypes.byref(shape), ctypes.byref(weights), _ptr(x), _ptr(token_ids), T,
-                                         _ptr(out), _stream(stream)), "moe_layer_forward_static")
+    T, px, pt, po = _batch(shape, x, token_ids, out)
+    _check(_lib.moe_layer_forward_static(ctypes.byref(shape), ctypes.byref(weights), px, pt, T, po,
+                                         _stream(stream)), "moe_layer_forward_static")
     return out
 
 
@@ -195,9 +232,8 @@ class Context:
         _check(_lib.moe_prepare(self._h, ctypes.byref(canonical), _stream(stream)), "moe_prepare")
 
     def forward(self, x, token_ids, out, stream=None):
-        T = x.shape[0] if x.dim() == 2 else 0
-        _check(_lib.moe_ctx_forward(self._h, _ptr(x), _ptr(token_ids), T, _ptr(out), _stream(stream)),
-               "moe_ctx_forward")
+        T, px, pt, po = _batch(self.shape, x, token_ids, out)
+        _check(_lib.moe_ctx_forward(self._h, px, pt, T, po, _stream(stream)), "moe_ctx_forward")
         return out
 
     def flags(self, reset: bool = False, stream=None) -> int:

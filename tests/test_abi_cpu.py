@@ -183,3 +183,41 @@ def test_static_forward_refuses_before_touching_the_device():
     assert L.moe_layer_forward_static(ctypes.byref(s), ctypes.byref(w), FAKE, None, 0, FAKE * 3, None) == OK
     # out overlapping x
     assert L.moe_layer_forward_static(ctypes.byref(s), ctypes.byref(w), FAKE, None, 4, FAKE + 16, None) == INVALID
+
+
+def test_binding_checks_caller_tensors_before_any_call():
+    """The Python binding passes plain pointers, so it checks what the C ABI
+    cannot: x and out [T, hidden] fp32, token_ids [T] int32, dense layout and
+    GPU memory.  Each bad argument raises ValueError before the library is
+    called (these tensors are on the CPU, the last check every case reaches
+    when its shape and type are right)."""
+    import torch
+
+    s = shape()
+    w = good_weights()
+    H = s.hidden
+    ws = torch.zeros(64, dtype=torch.uint8)
+    x = torch.zeros(4, H)
+    out = torch.zeros(4, H)
+    tok = torch.zeros(4, dtype=torch.int32)
+    cases = [
+        (dict(x=torch.zeros(H)), "x: expected"),
+        (dict(x=torch.zeros(4, H + 32)), "x: expected shape"),
+        (dict(x=torch.zeros(4, H, dtype=torch.float64)), "x: expected torch.float32"),
+        (dict(x=torch.zeros(H, 4).t()), "x: must be contiguous"),
+        (dict(out=torch.zeros(3, H)), "out: expected shape"),
+        (dict(token_ids=torch.zeros(5, dtype=torch.int32)), "token_ids: expected shape"),
+        (dict(token_ids=torch.zeros(4, dtype=torch.int64)), "token_ids: expected torch.int32"),
+        (dict(), "x: must be in GPU memory"),
+    ]
+    for change, msg in cases:
+        a = dict(x=x, token_ids=tok, out=out)
+        a.update(change)
+        with pytest.raises(ValueError, match=msg):
+            qr.layer_forward(s, w, a["x"], a["token_ids"], a["out"], ws)
+        with pytest.raises(ValueError, match=msg):
+            qr.layer_forward_static(s, w, a["x"], a["token_ids"], a["out"])
+    with pytest.raises(ValueError, match="workspace: must be in GPU memory"):
+        qr.workspace_init(ws)
+    with pytest.raises(ValueError, match="table: must be in GPU memory"):
+        qr.check_hash_table(torch.zeros(8, 4, dtype=torch.int32), 16, ws)
