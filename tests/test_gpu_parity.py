@@ -229,6 +229,9 @@ SMALL = [
     ms.LayerConfig("q2_h2048_f1024_T80", 2048, 16, 4, 1024, 80, routed_fmt="q2", seed=89),
     ms.LayerConfig("q8_f4096_T70", 512, 16, 2, 4096, 70, seed=90),
     ms.LayerConfig("q8_h4096_f1024_T1", 4096, 16, 2, 1024, 1, seed=91),
+    # the one-token down kernel's widest instances: ffn 4096 with eight routed slots
+    ms.LayerConfig("q8_top8_f4096_T1", 512, 32, 8, 4096, 1, seed=92),
+    ms.LayerConfig("q2_top8_f4096_T1", 512, 32, 8, 4096, 1, routed_fmt="q2", seed=93),
 ]
 
 
