@@ -118,7 +118,9 @@ def check(cfg, inp, g, x=None, tok=None, rows=None, stride=0, name=""):
     out_g, out_o = g["out"][rows], o["out"]
     assert np.all(np.isfinite(out_g))
     scale = float(np.max(np.abs(out_o)))
-    err = float(np.max(np.abs(out_g.astype(np.float64) - out_o))) / scale
+    err = float(np.max(np.abs(out_g.astype(np.float64) - out_o)))
+    # normwise; an all-zero reference (only zero tokens sampled) must be met exactly
+    err = err / scale if scale > 0 else (0.0 if err == 0 else float("inf"))
     # h codes of the sampled pairs: equal except single steps at rounding boundaries
     S = k + 1 if cfg.shared else k
     n_h, n_bad, hd_rel = 0, 0, 0.0
@@ -240,6 +242,29 @@ def test_small_parity(cfg):
     inp, layer = case(cfg)
     g = run_gpu(cfg, inp, layer, stride=1)
     check(cfg, inp, g, stride=1)
+
+
+@pytest.mark.parametrize("T,fmt", [(1, "q8"), (6, "q8"), (40, "q8"), (300, "q8"), (1, "q2"), (80, "q2")])
+def test_degenerate_activations(T, fmt):
+    """Blocks whose quantization scale is zero and saturated routing, on each
+    path: a token of zeros (every x and h block has amax 0, so d = 0 and every
+    code 0; its output is exactly zero), two zero 32-blocks inside another
+    token, and tokens scaled by 1e3 (router sigmoids saturate to 0 or 1, gate
+    values far below -89 give h = -0)."""
+    cfg = ms.LayerConfig(f"degenerate_{fmt}_T{T}", 512, 16, 4, 512, T, routed_fmt=fmt, seed=95 + T)
+    inp = ms.make_inputs(cfg)
+    x = inp["x"].copy()
+    x[0] = 0.0
+    if T > 1:
+        x[1, 32:96] = 0.0
+    if T > 2:
+        x[2:T:3] *= 1000.0
+    layer = _qr().MoELayer(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared, cfg.routed_fmt, cfg.route,
+                           0).load(inp)
+    g = run_gpu(cfg, inp, layer, x=x, stride=1)
+    check(cfg, inp, g, x=x, stride=1)
+    assert not np.any(g["out"][0]), "a zero token's output is exactly zero"
+    assert not np.any(g["xq"][0]) and not np.any(g["xd"][0])
 
 
 def test_every_token_to_the_same_experts():
