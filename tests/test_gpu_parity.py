@@ -231,6 +231,13 @@ SMALL = [
     ms.LayerConfig("q2_h2048_f1024_T80", 2048, 16, 4, 1024, 80, routed_fmt="q2", seed=89),
     ms.LayerConfig("q8_f4096_T70", 512, 16, 2, 4096, 70, seed=90),
     ms.LayerConfig("q8_h4096_f1024_T1", 4096, 16, 2, 1024, 1, seed=91),
+    # expert counts that fill no tile or wave evenly, and learned top-1
+    ms.LayerConfig("e100_top5_T1", 512, 100, 5, 256, 1, seed=110),
+    ms.LayerConfig("e100_top5_T7", 512, 100, 5, 256, 7, seed=111),
+    ms.LayerConfig("e100_top5_T230", 512, 100, 5, 256, 230, seed=112),
+    ms.LayerConfig("q2_e100_hash_T33", 512, 100, 5, 512, 33, routed_fmt="q2", route="hash", vocab=500, seed=113),
+    ms.LayerConfig("top1_T1", 512, 16, 1, 256, 1, seed=114),
+    ms.LayerConfig("top1_T70", 512, 16, 1, 256, 70, seed=115),
     # the one-token down kernel's widest instances: ffn 4096 with eight routed slots
     ms.LayerConfig("q8_top8_f4096_T1", 512, 32, 8, 4096, 1, seed=92),
     ms.LayerConfig("q2_top8_f4096_T1", 512, 32, 8, 4096, 1, routed_fmt="q2", seed=93),
