@@ -580,8 +580,8 @@ def cpu_baseline(cfg, inp, seconds, threads):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(multi-GPU expert parallelism is designed, not built)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the layer's expert-parallel split over several GPUs is a design, not code)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
